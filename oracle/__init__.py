@@ -1,0 +1,25 @@
+"""CPU oracle of one MoE layer (forward and backward) and of its MXFP8 format.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import or run anything here.  The GPU
+library (``mixture_experts_layer_offsets_amd``) shares no code with it and
+never calls it: the oracle exists to check that library.
+
+Modules:
+  numerics  bf16 / fp32 rounding points
+  mx        E4M3 + E8M0 block quantiser (OCP Microscaling conversion)
+  layer     router, top-k, layout, dispatch, SwiGLU experts, combine, backward,
+            plus a per-token brute-force evaluator and a sampled weight-gradient
+            evaluator for sizes the full oracle cannot finish
+
+Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
+something other than itself (hand-computed fixtures, closed forms, library
+routines, brute force, finite differences, an independent autograd
+formulation), except the MX recipe of the backward pass, which is a
+self-consistent definition ("parity unpinned" for that recipe choice; its
+arithmetic is still pinned through the quantiser and the bf16 path).
+"""
+from . import layer, mx, numerics  # noqa: F401
+from .layer import (TokenEvaluator, backward, combine, dispatch,  # noqa: F401
+                    expert_weight_grad_columns, forward, layout, router_backward,
+                    router_logits, topk_softmax)

@@ -1,0 +1,107 @@
+"""MXFP8 quantiser of the oracle: E4M3 elements with one E8M0 scale per 32.
+
+Test infrastructure only: nothing in the GPU library imports this module.
+
+The pages say only that MXFP8 activation quantisation is fused into the
+dispatch, grouped-GEMM and SwiGLU data paths (kucoin.com news flash "O MoK do
+Cursor alcança aumento de desempenho de 2,37x no NVIDIA GB300 NVL72",
+section 02; deepdigest.ru article on MoK).  The format itself is the OCP
+Microscaling one: a block of 32 values shares a power-of-two scale stored as
+an 8-bit biased exponent (E8M0, bias 127), and each value is an FP8 E4M3
+number (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+max normal 448, S.1111.111 is NaN).
+
+Conversion of one block v[0..31] (the reading used throughout):
+  amax = max |v_i|
+  amax == 0  ->  scale code 0, every element code 0
+  otherwise  s = clamp(floor(log2 amax) - 8, -127, 127)   (8 = E4M3's emax)
+             scale code = s + 127
+             q_i = E4M3(clamp(v_i * 2^-s, -448, 448)), nearest, ties to even,
+                   gradual underflow into the subnormals (quantum 2^-9)
+  dequantised value = E4M3value(q_i) * 2^s (exact in fp32 and bf16)
+The sign bit of a code is set exactly when the value is < 0, so a negative
+value that rounds to zero keeps a sign (0x80) and +0/-0 inputs give 0x00.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+BLOCK = 32
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Encode values with |v| <= 448 to E4M3 codes (uint8), nearest-even."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(a)):
+        raise ValueError("e4m3_encode: value outside [-448, 448]")
+    code = np.zeros(v.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # Below the smallest normal the spacing is 2^-9; q = 8 lands exactly on
+    # 2^-6, whose code (exponent field 1, mantissa 0) is also 8.
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)
+    nrm = ~sub
+    _, ex = np.frexp(a[nrm])          # a = m * 2^ex with m in [0.5, 1)
+    e = ex.astype(np.int64) - 1       # a in [2^e, 2^(e+1))
+    q = np.rint(np.ldexp(a[nrm], 3 - e)).astype(np.int64)  # in [8, 16]
+    up = q == 16
+    q[up] = 8
+    e[up] += 1
+    code[nrm] = ((e + 7) << 3) | (q - 8)
+    code |= (v < 0).astype(np.int64) << 7
+    return code.astype(np.uint8)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of E4M3 codes (fp64); the NaN codes decode to NaN."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = c & 0x7
+    mag = np.where(ex == 0, np.ldexp(man.astype(np.float64), -9),
+                   np.ldexp((8 + man).astype(np.float64), ex - 10))
+    mag = np.where((ex == 15) & (man == 7), np.nan, mag)
+    return sign * mag
+
+
+def e8m0_decode(code) -> np.ndarray:
+    """2^(code - 127) as fp64 (code 255, the NaN code, is never produced)."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    return np.ldexp(1.0, c - 127)
+
+
+def mx_quantize(v, axis: int = -1):
+    """Quantise ``v`` in blocks of 32 along ``axis``.
+
+    Returns (codes uint8, same shape as v; scales uint8, that axis divided by 32).
+    """
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    n = v.shape[-1]
+    if n % BLOCK:
+        raise ValueError(f"mx_quantize: axis length {n} is not a multiple of {BLOCK}")
+    b = v.reshape(v.shape[:-1] + (n // BLOCK, BLOCK))
+    amax = np.max(np.abs(b), axis=-1)
+    _, ex = np.frexp(amax)
+    e = ex.astype(np.int64) - 1                 # floor(log2 amax) for amax > 0
+    s = np.clip(e - 8, -127, 127)
+    s = np.where(amax == 0, -127, s)
+    scaled = np.clip(np.ldexp(b, -s[..., None]), -E4M3_MAX, E4M3_MAX)
+    codes = e4m3_encode(scaled).reshape(v.shape)
+    scales = (s + 127).astype(np.uint8)
+    return np.moveaxis(codes, -1, axis), np.moveaxis(scales, -1, axis)
+
+
+def mx_dequantize(codes, scales, axis: int = -1) -> np.ndarray:
+    """Inverse of :func:`mx_quantize` (exact)."""
+    c = np.moveaxis(np.asarray(codes, dtype=np.uint8), axis, -1)
+    s = np.moveaxis(np.asarray(scales, dtype=np.uint8), axis, -1)
+    vals = e4m3_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // BLOCK, BLOCK))
+    out = vals * e8m0_decode(s)[..., None]
+    return np.moveaxis(out.reshape(c.shape), -1, axis)
+
+
+def mx_roundtrip(v, axis: int = -1) -> np.ndarray:
+    """deq(MXQ(v)): the value a consumer of the quantised tensor sees."""
+    c, s = mx_quantize(v, axis)
+    return mx_dequantize(c, s, axis)
