@@ -1,0 +1,235 @@
+"""Benchmark: one MoE layer, forward + backward, on one MI355X.
+
+A step is one pass of the whole layer -- routing/layout, dispatch, expert FFN
+(grouped GEMMs with fused SwiGLU), combine, and the full backward -- over one
+batch of seeded synthetic inputs already resident in HBM.  Prints ONE JSON
+line.  The default workload is the Kimi-shaped expert share: 2048 tokens x
+top-8 = 16,384 routed rows, hidden 7168, 6 local experts of intermediate 2048,
+Zipf(s=1.0) expert loads, bf16.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+FWD_STAGES = ["route+layout", "dispatch", "gemm_gate_up_swiglu", "gemm_down", "shared",
+              "combine"]
+BWD_STAGES = ["reverse_combine", "gemm_dgrad_down_swiglu_bwd", "gemm_wgrad_down",
+              "gemm_dgrad_gate_up", "gemm_wgrad_gate_up", "shared_bwd",
+              "router_bwd+reverse_dispatch"]
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="kimi-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=96,
+                    help="tokens of the bounded oracle sample (CPU baseline)")
+    return ap.parse_args()
+
+
+def _algorithmic(w):
+    """Algorithmic flops / bytes of the layer's stages (per step)."""
+    R, T, H, I, k = w.T * w.k, w.T, w.H, w.I, w.k
+    f = {
+        "gemm_gate_up_swiglu": 4.0 * R * H * I,
+        "gemm_down": 2.0 * R * H * I,
+        "gemm_dgrad_down_swiglu_bwd": 2.0 * R * H * I,
+        "gemm_wgrad_down": 2.0 * R * H * I,
+        "gemm_dgrad_gate_up": 4.0 * R * H * I,
+        "gemm_wgrad_gate_up": 4.0 * R * H * I,
+    }
+    b = {
+        # unique token rows read once, routed rows written once, + indices
+        "dispatch": T * H * 2 + R * H * 2 + R * 4,
+        # routed rows read once, token rows written once, + weights/indices
+        "combine": R * H * 2 + T * H * 2 + R * 8,
+        # dOut read once, Y read for dw, dY written, + weights/indices/dw
+        "reverse_combine": T * H * 2 + 2 * R * H * 2 + R * 12,
+    }
+    return f, b
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = os.path.join(ROOT, "mixture_experts_layer_offsets_amd", "csrc", "gemm.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        ent = rec.get(kernel)
+        if not ent or ent.get("gemm_hip_sha256") != sha:
+            return None
+        return ent["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, inp, tokens: int):
+    """The oracle, as it is, on a bounded sample: the first `tokens` tokens of
+    the same workload (same weights and routing), forward + backward."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    sub = dict(inp)
+    for key in ("x", "dout", "topk_idx", "topk_w"):
+        if sub.get(key) is not None:
+            sub[key] = np.ascontiguousarray(inp[key][:tokens])
+    t0 = time.perf_counter()
+    fw = oracle.forward(sub, w.k, mx=w.mx)
+    oracle.backward(sub, fw)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {tokens} of {w.T} tokens ({tokens * w.k} routed rows) of the "
+                      f"same workload, fp64 numpy oracle, forward+backward, {dt:.1f} s"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from mixture_experts_layer_offsets_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_layer_offsets_amd import build
+        build.build(verbose=False)
+    import mixture_experts_layer_offsets_amd as m
+
+    w = synth.workload(a.workload)
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            x = x.view(np.int16)
+        return torch.from_numpy(x).to(dev)
+
+    shape = m.Shape(w.T, w.H, w.E, w.k, w.I, w.shared_I, m.MOE_MXFP8 if w.mx else m.MOE_BF16)
+    layer = m.MoeLayer(shape, dev)
+    layer.prepare(d(inp["w_gate"]), d(inp["w_up"]), d(inp["w_down"]), d(inp["ws_gate"]),
+                  d(inp["ws_up"]), d(inp["ws_down"]))
+    x, wr, bias = d(inp["x"]), d(inp["w_router"]), d(inp["bias"])
+    idx, tw, dout = d(inp["topk_idx"]), d(inp["topk_w"]), d(inp["dout"])
+    out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
+    grads = layer.grad_buffers(router=wr is not None)
+
+    n_f, n_b = len(FWD_STAGES) + 1, len(BWD_STAGES) + 1
+
+    def make_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()
+        return evs
+
+    def sched_for(evs):
+        import ctypes
+        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        s = m.MoeSched()
+        s.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        s.n_stage_events = len(evs)
+        return s, arr
+
+    def step(sf=None, sb=None):
+        layer.forward(x, w_router=wr, bias=bias, topk_idx=idx, topk_w=tw, out=out, sched=sf)
+        if w.backward:
+            layer.backward(dout, x, w_router=wr, grads=grads, sched=sb)
+
+    for _ in range(a.warmup):
+        step()
+    ev = [(make_events(n_f), make_events(n_b)) for _ in range(a.steps)]
+    scheds = [(sched_for(f), sched_for(b)) for f, b in ev]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for (sf, _), (sb, _) in scheds:
+        step(sf, sb)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / a.steps * 1e3
+
+    stage_ms = {}
+    for i, name in enumerate(FWD_STAGES):
+        stage_ms[name] = float(np.mean([f[i].elapsed_time(f[i + 1]) for f, _ in ev]))
+    if w.backward:
+        for i, name in enumerate(BWD_STAGES):
+            stage_ms[name] = float(np.mean([b[i].elapsed_time(b[i + 1]) for _, b in ev]))
+    flops, byts = _algorithmic(w)
+    mfma = {k: flops[k] / (stage_ms[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+            for k in flops if k in stage_ms and stage_ms[k] > 0}
+    hbm = {k: byts[k] / (stage_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS
+           for k in byts if k in stage_ms and stage_ms[k] > 0}
+
+    dom = "gemm_gate_up_swiglu"
+    achieved = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    traffic = _traffic("grouped_gemm_kernel<false, true, 2>")
+    tokens_per_step = w.T
+    res = {
+        "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X" if w.backward
+                  else "MoE layer fwd tokens/s on 1 MI355X",
+        "value": tokens_per_step * a.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8" if w.mx else "bf16",
+        "data": "synthetic (seeded; random-init weights; supplied Zipf routing)"
+                if w.routing == "supplied" else "synthetic (seeded; random-init weights)",
+        "config": {"workload": f"{w.name}: T={w.T} tokens, top-{w.k} ({w.T * w.k} routed rows), "
+                               f"hidden {w.H}, {w.E} experts of intermediate {w.I}"
+                               + (f", shared expert {w.shared_I}" if w.shared_I else "")
+                               + (f", Zipf s={w.zipf_s}" if w.routing == "supplied" else ""),
+                   "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k,
+                   "inter": w.I, "routed_rows": w.T * w.k},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<false, true, 2> "
+                     "(gate/up GEMM + SwiGLU epilogue)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "avg_launch_ms": stage_ms[dom]},
+        "stage_ms": stage_ms,
+        "mfma_frac": mfma,
+        "hbm_frac": hbm,
+        "layer_fwd_ms": sum(stage_ms[n] for n in FWD_STAGES),
+        "layer_bwd_ms": sum(stage_ms[n] for n in BWD_STAGES) if w.backward else None,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, min(a.cpu_tokens, w.T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,251 @@
+/*
+ * moe.h -- C ABI of libmoe: one Mixture-of-Experts layer, forward and
+ * backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (the pages describe the layer in prose only):
+ *   [KC] kucoin.com news flash "O MoK do Cursor alcança aumento de desempenho
+ *        de 2,37x no NVIDIA GB300 NVL72", §01 "O imposto sobre comunicações
+ *        do MoE", §02 (pull dispatch, megakernel, ring buffer), §03
+ *        (benchmark: "Schedule, Dispatch, Expert FFN, Combine e a fusão
+ *        ponderada final").
+ *   [NA] noticiai.com.br "Cursor abre código do Mixture-of-Kittens: kernel
+ *        MoE que acelera treinamento em GPUs Blackwell em até 2,37×",
+ *        section "As três decisões de design que fazem a diferença".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device buffers must be device memory of the current
+ *   HIP device; all other pointers (shapes, schedules, status) are host.
+ * - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ * - Shapes: T tokens, H hidden, E routed experts, k top-k, I expert
+ *   intermediate size, R = T*k routed rows, Is shared-expert intermediate.
+ *   Expert weights are row-major with the layer computing x*W:
+ *   w_gate, w_up [E][H][I]; w_down [E][I][H]; router [H][E].
+ * - Rows: f = t*k + j is the flat (token, slot) index; r is the row in
+ *   expert-sorted order.  perm[r] = f and inv_perm[f] = r.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every call only enqueues work on it and returns; no call waits for the
+ *   device (the only exception is moe_read_status).  Inputs must stay
+ *   unchanged and outputs unread until the stream has passed the call.
+ * - The library allocates no device memory and keeps no state between
+ *   calls: scratch comes from the caller's workspace (`ws`, `ws_bytes`,
+ *   sized by moe_workspace_bytes) and the forward->backward context from
+ *   the caller's `saved` buffer (moe_saved_bytes).  Calls on one stream with
+ *   distinct workspaces may be issued from several threads.
+ * - Results are deterministic: the same inputs give bitwise-identical
+ *   outputs, run to run (no floating-point atomics; every reduction has a
+ *   fixed order).
+ * - No token is dropped and no buffer depends on the routing: every (t, j)
+ *   owns one row ([NA] "Buffer em anel elimina a CPU do loop").
+ * - Errors: each int-returning call returns MOE_OK or one of the codes
+ *   below and enqueues nothing when it fails its argument checks.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* NULL required pointer, size <= 0, k > E when routing, overflow */
+  MOE_ERR_UNSUPPORTED = 2,   /* shape outside the kernels' limits (see moe_shape) */
+  MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4,           /* a HIP launch or copy failed */
+  MOE_ERR_DEVICE_TIMEOUT = 5 /* reported by moe_read_status only */
+};
+
+enum { MOE_BF16 = 0, MOE_MXFP8 = 1 };
+
+/* The layer's shape, following the quantities the pages tune the layer by:
+ * hidden size, top-k and expert count [KC §03], expert intermediate size
+ * [KC §02], plus the token count and the datatype.
+ * Limits: 1 <= T; 1 <= k; 1 <= E <= 1024; H and I multiples of 64 (and of
+ * 32 for MXFP8, implied); R = T*k < 2^31; shared_inter 0 or a multiple of 64. */
+typedef struct moe_shape {
+  int32_t tokens;       /* T */
+  int32_t hidden;       /* H */
+  int32_t experts;      /* E: routed experts held by this GPU */
+  int32_t top_k;        /* k */
+  int32_t inter;        /* I */
+  int32_t shared_inter; /* Is of the one shared expert; 0 = no shared expert */
+  int32_t dtype;        /* MOE_BF16 or MOE_MXFP8 */
+} moe_shape;
+
+/* Schedule knobs of the layer call.  The pages retune the minibatch and the
+ * number of communication processors per model shape [KC §03]; 0 always
+ * means "library default".
+ *
+ * stage_events (optional, host array of caller-created hipEvent_t, cast to
+ * void*): when non-NULL the layer calls record event i on `stream` at stage
+ * boundary i, for i < n_stage_events, so a caller can time each stage:
+ *   forward : 0 start, 1 routing+layout done, 2 dispatch done, 3 gate/up
+ *             GEMM + SwiGLU done, 4 down GEMM done, 5 shared expert done,
+ *             6 combine done;
+ *   backward: 0 start, 1 reverse-combine done, 2 down data-gradient GEMM
+ *             (+ SwiGLU backward) done, 3 down weight-gradient GEMM done,
+ *             4 gate/up data-gradient GEMM done, 5 gate/up weight-gradient
+ *             GEMM done, 6 shared expert done, 7 router + reverse-dispatch
+ *             done. */
+typedef struct moe_sched {
+  int32_t minibatch_rows; /* routed rows per minibatch (0 = default) */
+  int32_t ring_slots;     /* slots of the on-device ring (0 = default) */
+  int32_t comm_cus;       /* CUs given to dispatch/combine (0 = default) */
+  int32_t use_megakernel; /* 0 = staged kernels, 1 = persistent pipelined kernel */
+  void **stage_events;    /* hipEvent_t[n_stage_events] or NULL */
+  int32_t n_stage_events;
+} moe_sched;
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Bytes of scratch every call below needs at most for this shape (host call,
+ * no device work).  Depends only on the shape, never on the routing. */
+size_t moe_workspace_bytes(const moe_shape *shape);
+
+/* Bytes of the forward->backward context written by moe_layer_fwd. */
+size_t moe_saved_bytes(const moe_shape *shape);
+
+/* Bytes of the packed weights written by moe_prepare_weights. */
+size_t moe_packed_weight_bytes(const moe_shape *shape);
+
+/* ---------------------------------------------------------------- weights */
+
+/* Repack the expert weights into the layouts the grouped GEMMs read (the
+ * grouped GEMM wants expert-ordered, contraction-contiguous operands
+ * [KC §01]).  Inputs (device, bf16): w_gate, w_up [E][H][I], w_down
+ * [E][I][H]; the shared expert's ws_gate, ws_up [H][Is], ws_down [Is][H]
+ * (all three NULL when shared_inter == 0).  Output: `packed` (device,
+ * moe_packed_weight_bytes, caller-owned, opaque).  With MXFP8 the packed
+ * buffer also holds E4M3+E8M0 copies quantised along each GEMM's
+ * contraction axis.  Call again whenever the weights change. */
+int moe_prepare_weights(const moe_shape *shape, const uint16_t *w_gate,
+                        const uint16_t *w_up, const uint16_t *w_down,
+                        const uint16_t *ws_gate, const uint16_t *ws_up,
+                        const uint16_t *ws_down, void *packed, void *stream);
+
+/* ------------------------------------------------------------- the steps */
+
+/* Router logits: logits[t][e] = fp32(sum_h x[t][h] * w_router[h][e]) +
+ * bias[e] (bias may be NULL).  The router re-decides every step which
+ * experts a token visits [KC §01].  x [T][H] bf16, w_router [H][E] bf16,
+ * logits [T][E] fp32 (all device). */
+int moe_router_logits(const moe_shape *shape, const uint16_t *x,
+                      const uint16_t *w_router, const float *bias,
+                      float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Top-k selection and weights: per token, the k largest logits (equal
+ * logits: lower expert index first), slot j = j-th largest; weights =
+ * softmax over the k selected logits, in fp32.  Each token picks a few
+ * experts [KC §01].  logits [T][E] fp32 -> topk_idx [T][k] int32,
+ * topk_w [T][k] fp32.  Requires k <= E. */
+int moe_route(const moe_shape *shape, const float *logits, int32_t *topk_idx,
+              float *topk_w, void *stream);
+
+/* Layout ("Schedule"): count rows per expert, prefix-sum them, and order
+ * rows expert-contiguously, stable in f [KC §01].  topk_idx [T][k] int32
+ * (every entry in [0, E); duplicates within a token allowed) ->
+ * counts [E], offsets [E+1], perm [R], inv_perm [R] (int32, device).
+ * Bit-exact and deterministic.  Entries outside [0, E) are not checked on
+ * the host; the kernels clamp them into [0, E) and the result is then
+ * undefined but memory-safe. */
+int moe_layout(const moe_shape *shape, const int32_t *topk_idx,
+               int32_t *counts, int32_t *offsets, int32_t *perm,
+               int32_t *inv_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch (gather-permute): row r of x_perm is a copy of token
+ * perm[r] / k of x -- the destination-driven read the pages call pull
+ * dispatch [KC §02].  bf16: x_perm is uint16_t [R][H], x_scale unused.
+ * MXFP8: x_perm is E4M3 codes uint8 [R][H] and x_scale E8M0 uint8
+ * [R][H/32], quantised along H as the row is copied [KC §02]. */
+int moe_dispatch(const moe_shape *shape, const uint16_t *x,
+                 const int32_t *perm, void *x_perm, uint8_t *x_scale,
+                 void *stream);
+
+/* Expert FFN as grouped GEMMs over the expert-contiguous rows [KC §01]:
+ * for the rows [offsets[e], offsets[e+1]) of expert e,
+ * a = silu(X w_gate[e]) * (X w_up[e]) (SwiGLU fused in the GEMM epilogue),
+ * y = a w_down[e].  x_perm/x_scale as written by moe_dispatch, offsets
+ * [E+1], packed from moe_prepare_weights, y [R][H] bf16 (device).  The
+ * intermediate activations live in the workspace. */
+int moe_expert_ffn(const moe_shape *shape, const void *x_perm,
+                   const uint8_t *x_scale, const int32_t *offsets,
+                   const void *packed, uint16_t *y, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* Combine and final weighted fusion [KC §03]: out[t] = bf16( sum_{j<k}
+ * topk_w[t][j] * y[inv_perm[t*k+j]] + y_shared[t] ), fp32 accumulation in
+ * ascending j.  y [R][H], y_shared [T][H] (may be NULL), out [T][H] bf16. */
+int moe_combine(const moe_shape *shape, const uint16_t *y,
+                const float *topk_w, const int32_t *inv_perm,
+                const uint16_t *y_shared, uint16_t *out, void *stream);
+
+/* ------------------------------------------------------------- the layer */
+
+/* Whole forward: [router logits, top-k] or supplied routing, layout,
+ * dispatch, expert FFN (+ the shared expert), combine.
+ * Routing: pass w_router (+ optional bias) with topk_idx_in = topk_w_in =
+ * NULL, or pass topk_idx_in [T][k] / topk_w_in [T][k] (device) with
+ * w_router = NULL.  x [T][H] bf16, out [T][H] bf16, saved (device,
+ * moe_saved_bytes) receives the context moe_layer_bwd reads.  `sched` may
+ * be NULL (defaults). */
+int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched,
+                  const uint16_t *x, const uint16_t *w_router,
+                  const float *bias, const int32_t *topk_idx_in,
+                  const float *topk_w_in, const void *packed, uint16_t *out,
+                  void *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole backward, mirroring the forward's data movement [KC §01, §02]:
+ * reverse-combine, SwiGLU expert backward (data and weight gradients),
+ * reverse-dispatch, router backward.  dout [T][H] bf16; x and w_router as
+ * given to the forward (w_router NULL for supplied routing); saved from
+ * moe_layer_fwd.  Outputs (device): dx [T][H] bf16; dw_gate, dw_up
+ * [E][H][I] fp32; dw_down [E][I][H] fp32; dw_router [H][E] fp32 (router
+ * routing, else NULL); dws [H*Is | H*Is | Is*H] fp32 = shared expert's
+ * d(gate), d(up), d(down) (NULL without a shared expert); dtopk_w [T][k]
+ * fp32 = gradient of the routing weights (may be NULL).  Every output is
+ * fully written (experts that received no rows get zero gradients). */
+int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched,
+                  const uint16_t *dout, const uint16_t *x,
+                  const uint16_t *w_router, const void *saved,
+                  const void *packed, uint16_t *dx, float *dw_router,
+                  float *dw_gate, float *dw_up, float *dw_down, float *dws,
+                  float *dtopk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Device pointers into a forward context (host call, no device work):
+ * where moe_layer_fwd left each intermediate.  Any field may be NULL in
+ * the result when the shape has no such tensor. */
+typedef struct moe_saved_view {
+  int32_t *topk_idx;  /* [T][k] */
+  float *topk_w;      /* [T][k] */
+  float *logits;      /* [T][E] (router routing) */
+  int32_t *counts;    /* [E] */
+  int32_t *offsets;   /* [E+1] */
+  int32_t *perm;      /* [R] */
+  int32_t *inv_perm;  /* [R] */
+  void *x_perm;       /* bf16 [R][H], or E4M3 [R][H] */
+  uint8_t *x_scale;   /* E8M0 [R][H/32] (MXFP8) */
+  uint16_t *gu;       /* bf16 [R][2I]: g and u, interleaved in 32-column blocks */
+  uint16_t *act;      /* bf16 [R][I]: a (bf16) or its MX round trip (MXFP8) */
+  uint16_t *y;        /* bf16 [R][H] */
+  uint16_t *y_shared; /* bf16 [T][H] (shared expert) */
+} moe_saved_view;
+
+int moe_saved_pointers(const moe_shape *shape, void *saved,
+                       moe_saved_view *view);
+
+/* Reads the device status word of the last layer call that used `ws`
+ * (synchronises `stream`).  *status_host = MOE_OK or MOE_ERR_DEVICE_TIMEOUT. */
+int moe_read_status(const void *ws, int32_t *status_host, void *stream);
+
+/* Static description of an error code. */
+const char *moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,13 @@
+"""MI355X-native MoE layer (forward + backward): Python face of libmoe.
+
+``_lib`` exposes the C entry points of ``include/moe.h`` under the same names;
+``MoeLayer`` owns the caller-side buffers (workspace, saved context, packed
+weights) as torch tensors and calls those entry points.  All computation is in
+libmoe's HIP kernels.
+"""
+from ._lib import (MOE_BF16, MOE_MXFP8, MoeError, MoeSched, Shape, load,  # noqa: F401
+                   moe_combine, moe_dispatch, moe_expert_ffn, moe_layer_bwd, moe_layer_fwd,
+                   moe_layout, moe_packed_weight_bytes, moe_prepare_weights, moe_read_status,
+                   moe_route, moe_router_logits, moe_saved_bytes, moe_saved_pointers,
+                   moe_strerror, moe_workspace_bytes)
+from .layer import MoeLayer  # noqa: F401

@@ -1,0 +1,548 @@
+// libmoe C ABI: argument checks, carving of caller-owned buffers, and the
+// order of kernel launches for each entry point.  No entry point allocates
+// device memory or waits for the device (moe_read_status aside).
+//
+// The layer follows the parts the pages measure -- "Schedule, Dispatch,
+// Expert FFN, Combine e a fusão ponderada final" (kucoin.com news flash "O MoK
+// do Cursor alcança aumento de desempenho de 2,37x no NVIDIA GB300 NVL72",
+// §03) -- and its backward mirrors the forward's data movement (§01, §02).
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Sequential carver: the same code sizes a buffer (base == null) and hands
+// out its pieces, so sizes and offsets can never disagree.
+struct Carver {
+  char *base;
+  size_t off = 0;
+  explicit Carver(void *b) : base((char *)b) {}
+  template <class T>
+  T *take(size_t count) {
+    T *p = base ? (T *)(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+struct Dims {
+  long T, H, E, k, I, Is, R;
+  bool mx, shared;
+};
+
+int check_shape(const moe_shape *s, Dims *d) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->tokens < 1 || s->hidden < 1 || s->experts < 1 || s->top_k < 1 || s->inter < 1 ||
+      s->shared_inter < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
+  const long R = (long)s->tokens * s->top_k;
+  if (R >= (1L << 31)) return MOE_ERR_INVALID_ARG;
+  if (s->hidden % 64 || s->inter % 64 || s->shared_inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (s->experts > 1024 || s->top_k > 16) return MOE_ERR_UNSUPPORTED;
+  if ((long)s->hidden * s->experts >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;  // MX path: see moe_prepare_weights
+  d->T = s->tokens; d->H = s->hidden; d->E = s->experts; d->k = s->top_k; d->I = s->inter;
+  d->Is = s->shared_inter; d->R = R; d->mx = s->dtype == MOE_MXFP8; d->shared = s->shared_inter > 0;
+  return MOE_OK;
+}
+
+// ---- forward->backward context
+struct Saved {
+  int32_t *idx; float *w; float *logits;
+  int32_t *counts, *offsets, *tile_start, *order, *perm, *inv;
+  uint16_t *x_perm;   // bf16 rows (or the MX round trip of the rows)
+  uint16_t *gu, *act, *y;
+  uint16_t *gu_s, *act_s, *y_s;
+};
+
+size_t carve_saved(const Dims &d, void *base, Saved *s) {
+  Carver c(base);
+  Saved t{};
+  t.idx = c.take<int32_t>(d.R);
+  t.w = c.take<float>(d.R);
+  t.logits = c.take<float>(d.T * d.E);
+  t.counts = c.take<int32_t>(d.E);
+  t.offsets = c.take<int32_t>(d.E + 1);
+  t.tile_start = c.take<int32_t>(d.E + 1);
+  t.order = c.take<int32_t>(d.E);
+  t.perm = c.take<int32_t>(d.R);
+  t.inv = c.take<int32_t>(d.R);
+  t.x_perm = c.take<uint16_t>(d.R * d.H);
+  t.gu = c.take<uint16_t>(d.R * 2 * d.I);
+  t.act = c.take<uint16_t>(d.R * d.I);
+  t.y = c.take<uint16_t>(d.R * d.H);
+  if (d.shared) {
+    t.gu_s = c.take<uint16_t>(d.T * 2 * d.Is);
+    t.act_s = c.take<uint16_t>(d.T * d.Is);
+    t.y_s = c.take<uint16_t>(d.T * d.H);
+  }
+  if (s) *s = t;
+  return c.off;
+}
+
+// ---- per-call scratch
+struct Work {
+  int32_t *status;
+  int32_t *chunk_counts;
+  int32_t *dense_offsets, *dense_tiles, *dense_order;
+  // standalone layout / expert FFN
+  int32_t *tile_start, *order;
+  uint16_t *act, *gu;
+  // backward
+  uint16_t *dy, *dh, *dX, *wrT, *dh_s, *dxs;
+  float *dw, *dsel;
+};
+
+size_t carve_work(const Dims &d, void *base, Work *w) {
+  Carver c(base);
+  Work t{};
+  t.status = c.take<int32_t>(64);
+  const long nchunks = (d.R + kLayoutChunk - 1) / kLayoutChunk;
+  t.chunk_counts = c.take<int32_t>(nchunks * d.E);
+  t.dense_offsets = c.take<int32_t>(2);
+  t.dense_tiles = c.take<int32_t>(2);
+  t.dense_order = c.take<int32_t>(1);
+  t.tile_start = c.take<int32_t>(d.E + 1);
+  t.order = c.take<int32_t>(d.E);
+  const size_t union_start = c.off;
+  // forward-only pieces (standalone expert FFN)
+  t.act = c.take<uint16_t>(d.R * d.I);
+  t.gu = c.take<uint16_t>(d.R * 2 * d.I);
+  const size_t fwd_end = c.off;
+  // backward-only pieces share the same bytes
+  c.off = union_start;
+  t.dy = c.take<uint16_t>(d.R * d.H);
+  t.dh = c.take<uint16_t>(d.R * 2 * d.I);
+  t.dX = c.take<uint16_t>(d.R * d.H);
+  t.dw = c.take<float>(d.R);
+  t.dsel = c.take<float>(d.R);
+  t.wrT = c.take<uint16_t>(d.E * d.H);
+  if (d.shared) {
+    t.dh_s = c.take<uint16_t>(d.T * 2 * d.Is);
+    t.dxs = c.take<uint16_t>(d.T * d.H);
+  }
+  if (c.off < fwd_end) c.off = fwd_end;
+  if (w) *w = t;
+  return c.off;
+}
+
+// ---- packed weights
+struct Packed {
+  uint16_t *guT, *dT, *gu, *d;      // routed experts
+  uint16_t *sguT, *sdT, *sgu, *sd;  // shared expert
+};
+
+size_t carve_packed(const Dims &d, const void *base, Packed *p) {
+  Carver c((void *)base);
+  Packed t{};
+  t.guT = c.take<uint16_t>(d.E * 2 * d.I * d.H);  // [E][2I][H]
+  t.dT = c.take<uint16_t>(d.E * d.H * d.I);       // [E][H][I]
+  t.gu = c.take<uint16_t>(d.E * d.H * 2 * d.I);   // [E][H][2I]
+  t.d = c.take<uint16_t>(d.E * d.I * d.H);        // [E][I][H]
+  if (d.shared) {
+    t.sguT = c.take<uint16_t>(2 * d.Is * d.H);
+    t.sdT = c.take<uint16_t>(d.H * d.Is);
+    t.sgu = c.take<uint16_t>(d.H * 2 * d.Is);
+    t.sd = c.take<uint16_t>(d.Is * d.H);
+  }
+  if (p) *p = t;
+  return c.off;
+}
+
+int hip_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+hipStream_t S(void *s) { return (hipStream_t)s; }
+
+// Records the caller's stage event i (if any) on the stream.
+struct Stages {
+  const moe_sched *sc;
+  hipStream_t s;
+  void mark(int i) const {
+    if (sc && sc->stage_events && i < sc->n_stage_events && sc->stage_events[i])
+      hipEventRecord((hipEvent_t)sc->stage_events[i], s);
+  }
+};
+
+// Expert FFN over row-ragged groups: a = silu(X Wg) * (X Wu); y = a Wd.
+void ffn_forward(const uint16_t *X, long ldx, const int32_t *offsets, const int32_t *tiles,
+                 int G, long max_rows, long H, long I, const uint16_t *guT, const uint16_t *dT,
+                 uint16_t *act, uint16_t *gu, uint16_t *y, hipStream_t s,
+                 const Stages *st = nullptr, int mark = 0) {
+  GemmArgs p{};
+  p.A = X; p.lda = ldx;
+  p.B = guT; p.ldb = H; p.sB = 2 * I * H;
+  p.C = act; p.ldc = I;
+  p.C2 = gu; p.ldc2 = 2 * I;
+  p.offsets = offsets; p.tile_start = tiles;
+  p.G = G; p.N = (int)(2 * I); p.K = (int)H;
+  launch_gemm_rows(p, EPI_SWIGLU, true, (int)max_rows, s);
+  if (st) st->mark(mark);
+  GemmArgs q{};
+  q.A = act; q.lda = I;
+  q.B = dT; q.ldb = I; q.sB = H * I;
+  q.C = y; q.ldc = H;
+  q.offsets = offsets; q.tile_start = tiles;
+  q.G = G; q.N = (int)H; q.K = (int)I;
+  launch_gemm_rows(q, EPI_BF16, true, (int)max_rows, s);
+  if (st) st->mark(mark + 1);
+}
+
+// Backward of the expert FFN for row-ragged groups given dY (rows' output
+// gradient).  Writes dh (packed dg|du), dX, and the weight gradients.
+void ffn_backward(const uint16_t *X, long ldx, const uint16_t *dY, long lddy,
+                  const int32_t *offsets, const int32_t *tiles, const int32_t *order, int G,
+                  long max_rows, long H, long I, const uint16_t *gu_w, const uint16_t *d_w,
+                  const uint16_t *gu_saved, const uint16_t *act, uint16_t *dh, uint16_t *dX,
+                  float *dWg, float *dWu, float *dWd, hipStream_t s,
+                  const Stages *st = nullptr, int mark = 0) {
+  GemmArgs a{};  // dA = dY Wd^T, SwiGLU backward in the epilogue -> dh
+  a.A = dY; a.lda = lddy;
+  a.B = d_w; a.ldb = H; a.sB = I * H;
+  a.C = dh; a.ldc = 2 * I;
+  a.aux = gu_saved; a.ldaux = 2 * I;
+  a.offsets = offsets; a.tile_start = tiles;
+  a.G = G; a.N = (int)I; a.K = (int)H;
+  launch_gemm_rows(a, EPI_SWIGLU_BWD, true, (int)max_rows, s);
+  if (st) st->mark(mark);
+  GemmArgs b{};  // dWd = act^T dY
+  b.A = act; b.lda = I;
+  b.B = dY; b.ldb = lddy;
+  b.C = dWd; b.ldc = H; b.sC = I * H;
+  b.offsets = offsets; b.order = order;
+  b.G = G; b.M = (int)I; b.N = (int)H;
+  launch_gemm_wgrad(b, EPI_F32, s);
+  if (st) st->mark(mark + 1);
+  GemmArgs c{};  // dX = dh Wgu^T
+  c.A = dh; c.lda = 2 * I;
+  c.B = gu_w; c.ldb = 2 * I; c.sB = H * 2 * I;
+  c.C = dX; c.ldc = H;
+  c.offsets = offsets; c.tile_start = tiles;
+  c.G = G; c.N = (int)H; c.K = (int)(2 * I);
+  launch_gemm_rows(c, EPI_BF16, true, (int)max_rows, s);
+  if (st) st->mark(mark + 2);
+  GemmArgs e{};  // dWg | dWu = X^T dh
+  e.A = X; e.lda = ldx;
+  e.B = dh; e.ldb = 2 * I;
+  e.C = dWg; e.C2 = dWu; e.ldc = I; e.sC = H * I;
+  e.offsets = offsets; e.order = order;
+  e.G = G; e.M = (int)H; e.N = (int)(2 * I);
+  launch_gemm_wgrad(e, EPI_WGRAD_GU, s);
+  if (st) st->mark(mark + 3);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "shape or dtype not supported by the kernels";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or copy failed";
+    case MOE_ERR_DEVICE_TIMEOUT: return "device-side wait timed out";
+    default: return "unknown error";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape *shape) {
+  Dims d;
+  if (check_shape(shape, &d)) return 0;
+  return carve_work(d, nullptr, nullptr);
+}
+
+size_t moe_saved_bytes(const moe_shape *shape) {
+  Dims d;
+  if (check_shape(shape, &d)) return 0;
+  return carve_saved(d, nullptr, nullptr);
+}
+
+size_t moe_packed_weight_bytes(const moe_shape *shape) {
+  Dims d;
+  if (check_shape(shape, &d)) return 0;
+  return carve_packed(d, nullptr, nullptr);
+}
+
+int moe_prepare_weights(const moe_shape *shape, const uint16_t *w_gate, const uint16_t *w_up,
+                        const uint16_t *w_down, const uint16_t *ws_gate, const uint16_t *ws_up,
+                        const uint16_t *ws_down, void *packed, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!w_gate || !w_up || !w_down || !packed) return MOE_ERR_INVALID_ARG;
+  if (d.shared && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  Packed p;
+  carve_packed(d, packed, &p);
+  hipStream_t s = S(stream);
+  const int E = (int)d.E, H = (int)d.H, I = (int)d.I;
+  // forward gate/up: [E][2I][H], gate rows at 64-blocks' first half, up second
+  launch_transpose_pack(w_gate, p.guT, E, H, I, 2 * I, 64, 0, s);
+  launch_transpose_pack(w_up, p.guT, E, H, I, 2 * I, 64, 32, s);
+  launch_transpose_pack(w_down, p.dT, E, I, H, H, 32, 0, s);  // [E][H][I]
+  launch_interleave_copy(w_gate, p.gu, E, H, I, 2 * I, 64, 0, s);
+  launch_interleave_copy(w_up, p.gu, E, H, I, 2 * I, 64, 32, s);
+  if (hipMemcpyAsync(p.d, w_down, (size_t)d.E * d.I * d.H * 2, hipMemcpyDeviceToDevice, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  if (d.shared) {
+    const int Is = (int)d.Is;
+    launch_transpose_pack(ws_gate, p.sguT, 1, H, Is, 2 * Is, 64, 0, s);
+    launch_transpose_pack(ws_up, p.sguT, 1, H, Is, 2 * Is, 64, 32, s);
+    launch_transpose_pack(ws_down, p.sdT, 1, Is, H, H, 32, 0, s);
+    launch_interleave_copy(ws_gate, p.sgu, 1, H, Is, 2 * Is, 64, 0, s);
+    launch_interleave_copy(ws_up, p.sgu, 1, H, Is, 2 * Is, 64, 32, s);
+    if (hipMemcpyAsync(p.sd, ws_down, (size_t)d.Is * d.H * 2, hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return hip_status();
+}
+
+int moe_router_logits(const moe_shape *shape, const uint16_t *x, const uint16_t *w_router,
+                      const float *bias, float *logits, void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!x || !w_router || !logits || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.E % 8) return MOE_ERR_UNSUPPORTED;
+  Work w;
+  if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, (int)d.T, kTileM, s);
+  GemmArgs p{};
+  p.A = x; p.lda = d.H;
+  p.B = w_router; p.ldb = d.E; p.sB = 0;
+  p.C = logits; p.ldc = d.E;
+  p.bias = bias;
+  p.offsets = w.dense_offsets; p.tile_start = w.dense_tiles;
+  p.G = 1; p.N = (int)d.E; p.K = (int)d.H;
+  launch_gemm_rows(p, EPI_F32, false, (int)d.T, s);
+  return hip_status();
+}
+
+int moe_route(const moe_shape *shape, const float *logits, int32_t *topk_idx, float *topk_w,
+              void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (d.k > d.E) return MOE_ERR_INVALID_ARG;
+  launch_topk(logits, (int)d.T, (int)d.E, (int)d.k, topk_idx, topk_w, S(stream));
+  return hip_status();
+}
+
+int moe_layout(const moe_shape *shape, const int32_t *topk_idx, int32_t *counts,
+               int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes,
+               void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!topk_idx || !counts || !offsets || !perm || !inv_perm || !ws) return MOE_ERR_INVALID_ARG;
+  Work w;
+  if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  launch_layout(topk_idx, (int)d.R, (int)d.E, w.chunk_counts, counts, offsets, perm, inv_perm,
+                w.tile_start, kTileM, w.order, S(stream));
+  return hip_status();
+}
+
+int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *perm, void *x_perm,
+                 uint8_t *x_scale, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!x || !perm || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (d.mx) {
+    if (!x_scale) return MOE_ERR_INVALID_ARG;
+    launch_dispatch_mx(x, perm, (uint8_t *)x_perm, x_scale, nullptr, (int)d.R, (int)d.k,
+                       (int)d.H, S(stream));
+  } else {
+    launch_dispatch_bf16(x, perm, (uint16_t *)x_perm, (int)d.R, (int)d.k, (int)d.H, S(stream));
+  }
+  return hip_status();
+}
+
+int moe_expert_ffn(const moe_shape *shape, const void *x_perm, const uint8_t *x_scale,
+                   const int32_t *offsets, const void *packed, uint16_t *y, void *ws,
+                   size_t ws_bytes, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  (void)x_scale;
+  if (!x_perm || !offsets || !packed || !y || !ws) return MOE_ERR_INVALID_ARG;
+  Work w;
+  if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  Packed p;
+  carve_packed(d, packed, &p);
+  hipStream_t s = S(stream);
+  // the GEMM's tile prefix, derived on the device from the offsets
+  launch_tile_starts(offsets, (int)d.E, kTileM, w.tile_start, s);
+  ffn_forward((const uint16_t *)x_perm, d.H, offsets, w.tile_start, (int)d.E, d.R, d.H, d.I,
+              p.guT, p.dT, w.act, w.gu, y, s);
+  return hip_status();
+}
+
+int moe_combine(const moe_shape *shape, const uint16_t *y, const float *topk_w,
+                const int32_t *inv_perm, const uint16_t *y_shared, uint16_t *out, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!y || !topk_w || !inv_perm || !out) return MOE_ERR_INVALID_ARG;
+  launch_combine(y, topk_w, inv_perm, y_shared, out, (int)d.T, (int)d.k, (int)d.H, S(stream));
+  return hip_status();
+}
+
+int moe_saved_pointers(const moe_shape *shape, void *saved, moe_saved_view *view) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!saved || !view) return MOE_ERR_INVALID_ARG;
+  Saved s;
+  carve_saved(d, saved, &s);
+  memset(view, 0, sizeof(*view));
+  view->topk_idx = s.idx; view->topk_w = s.w; view->logits = s.logits;
+  view->counts = s.counts; view->offsets = s.offsets; view->perm = s.perm;
+  view->inv_perm = s.inv; view->x_perm = s.x_perm; view->x_scale = nullptr;
+  view->gu = s.gu; view->act = s.act; view->y = s.y; view->y_shared = s.y_s;
+  return MOE_OK;
+}
+
+int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t *x,
+                  const uint16_t *w_router, const float *bias, const int32_t *topk_idx_in,
+                  const float *topk_w_in, const void *packed, uint16_t *out, void *saved,
+                  void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  (void)sched;
+  if (!x || !packed || !out || !saved || !ws) return MOE_ERR_INVALID_ARG;
+  const bool router = w_router != nullptr;
+  if (router == (topk_idx_in != nullptr) || (topk_idx_in != nullptr) != (topk_w_in != nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (router && (d.k > d.E)) return MOE_ERR_INVALID_ARG;
+  if (router && d.E % 8) return MOE_ERR_UNSUPPORTED;
+  Work w;
+  if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  Saved sv;
+  carve_saved(d, saved, &sv);
+  Packed p;
+  carve_packed(d, packed, &p);
+  hipStream_t s = S(stream);
+  const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k;
+  const Stages st{sched, s};
+  st.mark(0);
+  launch_fill_i32(w.status, 1, MOE_OK, s);
+
+  // Schedule: routing then layout
+  if (router) {
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
+    GemmArgs lg{};
+    lg.A = x; lg.lda = H;
+    lg.B = w_router; lg.ldb = E;
+    lg.C = sv.logits; lg.ldc = E;
+    lg.bias = bias;
+    lg.offsets = w.dense_offsets; lg.tile_start = w.dense_tiles;
+    lg.G = 1; lg.N = E; lg.K = H;
+    launch_gemm_rows(lg, EPI_F32, false, T, s);
+    launch_topk(sv.logits, T, E, k, sv.idx, sv.w, s);
+  } else {
+    if (hipMemcpyAsync(sv.idx, topk_idx_in, d.R * sizeof(int32_t), hipMemcpyDeviceToDevice, s) !=
+            hipSuccess ||
+        hipMemcpyAsync(sv.w, topk_w_in, d.R * sizeof(float), hipMemcpyDeviceToDevice, s) !=
+            hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  launch_layout(sv.idx, (int)d.R, E, w.chunk_counts, sv.counts, sv.offsets, sv.perm, sv.inv,
+                sv.tile_start, kTileM, sv.order, s);
+  st.mark(1);
+  // Dispatch
+  launch_dispatch_bf16(x, sv.perm, sv.x_perm, (int)d.R, k, H, s);
+  st.mark(2);
+  // Expert FFN
+  ffn_forward(sv.x_perm, H, sv.offsets, sv.tile_start, E, d.R, d.H, d.I, p.guT, p.dT, sv.act,
+              sv.gu, sv.y, s, &st, 3);
+  if (d.shared) {
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
+    ffn_forward(x, H, w.dense_offsets, w.dense_tiles, 1, d.T, d.H, d.Is, p.sguT, p.sdT,
+                sv.act_s, sv.gu_s, sv.y_s, s);
+  }
+  st.mark(5);
+  // Combine + final weighted fusion
+  launch_combine(sv.y, sv.w, sv.inv, d.shared ? sv.y_s : nullptr, out, T, k, H, s);
+  st.mark(6);
+  return hip_status();
+}
+
+int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t *dout,
+                  const uint16_t *x, const uint16_t *w_router, const void *saved,
+                  const void *packed, uint16_t *dx, float *dw_router, float *dw_gate,
+                  float *dw_up, float *dw_down, float *dws, float *dtopk_w, void *ws,
+                  size_t ws_bytes, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  (void)sched;
+  if (!dout || !x || !saved || !packed || !dx || !dw_gate || !dw_up || !dw_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  const bool router = w_router != nullptr;
+  if (router && !dw_router) return MOE_ERR_INVALID_ARG;
+  if (d.shared && !dws) return MOE_ERR_INVALID_ARG;
+  Work w;
+  if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  Saved sv;
+  carve_saved(d, (void *)saved, &sv);
+  Packed p;
+  carve_packed(d, packed, &p);
+  hipStream_t s = S(stream);
+  const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k;
+  const Stages st{sched, s};
+  st.mark(0);
+  launch_fill_i32(w.status, 1, MOE_OK, s);
+
+  // Reverse-combine: dY rows, dw, and (router) the selected-logit gradient
+  float *dw = dtopk_w ? dtopk_w : w.dw;
+  launch_reverse_combine(dout, sv.y, sv.w, sv.inv, w.dy, dw, router ? w.dsel : nullptr, T, k, H,
+                         s);
+  st.mark(1);
+  // Expert FFN backward
+  ffn_backward(sv.x_perm, H, w.dy, H, sv.offsets, sv.tile_start, sv.order, E, d.R, d.H, d.I,
+               p.gu, p.d, sv.gu, sv.act, w.dh, w.dX, dw_gate, dw_up, dw_down, s, &st, 2);
+  if (d.shared) {
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
+    float *dWsg = dws, *dWsu = dws + d.H * d.Is, *dWsd = dws + 2 * d.H * d.Is;
+    ffn_backward(x, H, dout, H, w.dense_offsets, w.dense_tiles, w.dense_order, 1, d.T, d.H,
+                 d.Is, p.sgu, p.sd, sv.gu_s, sv.act_s, w.dh_s, w.dxs, dWsg, dWsu, dWsd, s);
+  }
+  st.mark(6);
+  // Router backward and reverse-dispatch
+  if (router) {
+    launch_transpose_pack(w_router, w.wrT, 1, H, E, E, 32, 0, s);
+    launch_router_wgrad(x, sv.perm, sv.offsets, w.dsel, dw_router, E, k, H, s);
+  }
+  launch_reverse_dispatch(w.dX, sv.inv, sv.idx, router ? w.dsel : nullptr,
+                          router ? w.wrT : nullptr, d.shared ? w.dxs : nullptr, dx, T, k, H, s);
+  st.mark(7);
+  return hip_status();
+}
+
+int moe_read_status(const void *ws, int32_t *status_host, void *stream) {
+  if (!ws || !status_host) return MOE_ERR_INVALID_ARG;
+  // the status word is the first carved piece of every workspace
+  if (hipMemcpyAsync(status_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost, S(stream)) !=
+          hipSuccess ||
+      hipStreamSynchronize(S(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

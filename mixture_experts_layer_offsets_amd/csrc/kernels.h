@@ -1,0 +1,84 @@
+// Host-side launchers of libmoe's kernels (all asynchronous on stream `s`).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kLayoutChunk = 1024;  // flat rows per block of the layout passes
+constexpr int kTileM = 256;         // rows of one grouped-GEMM tile
+constexpr int kTileN = 256;         // columns of one grouped-GEMM tile
+constexpr int kTileK = 64;          // contraction depth of one LDS stage
+
+// route_layout.hip
+void launch_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w,
+                 hipStream_t s);
+void launch_layout(const int32_t *idx, int R, int E, int32_t *chunk_counts, int32_t *counts,
+                   int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *tile_start,
+                   int tile_rows, int32_t *order, hipStream_t s);
+void launch_dense_groups(int32_t *offsets, int32_t *tile_start, int32_t *order, int M,
+                         int tile_rows, hipStream_t s);
+void launch_tile_starts(const int32_t *offsets, int G, int tile_rows, int32_t *tile_start,
+                        hipStream_t s);
+void launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
+
+// permute.hip
+void launch_dispatch_bf16(const uint16_t *x, const int32_t *perm, uint16_t *xp, int R, int k,
+                          int H, hipStream_t s);
+void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
+                        uint16_t *xhat, int R, int k, int H, hipStream_t s);
+void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
+                          hipStream_t s);
+void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,
+                    uint16_t *out, int T, int k, int H, hipStream_t s);
+void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float *w,
+                            const int32_t *inv, uint16_t *dy, float *dw, float *dsel, int T,
+                            int k, int H, hipStream_t s);
+void launch_reverse_dispatch(const uint16_t *dX, const int32_t *inv, const int32_t *idx,
+                             const float *dsel, const uint16_t *wrT, const uint16_t *dxs,
+                             uint16_t *dx, int T, int k, int H, hipStream_t s);
+void launch_router_wgrad(const uint16_t *x, const int32_t *perm, const int32_t *offsets,
+                         const float *dsel, float *dwr, int E, int k, int H, hipStream_t s);
+void launch_transpose_pack(const uint16_t *in, uint16_t *out, int G, int rows, int cols,
+                           int out_rows_total, int blk_stride, int blk_off, hipStream_t s);
+void launch_interleave_copy(const uint16_t *in, uint16_t *out, int G, int rows, int cols,
+                            int out_cols, int blk_stride, int blk_off, hipStream_t s);
+
+// gemm.hip: grouped GEMMs on MFMA (bf16 inputs, fp32 accumulation)
+enum EpiKind { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_WGRAD_GU = 4 };
+
+struct GemmArgs {
+  const uint16_t *A;
+  long lda;
+  const uint16_t *B;
+  long ldb;
+  long sB;          // per-group stride of B (row-ragged mode)
+  void *C;
+  long ldc;
+  long sC;          // per-group stride of C (weight-gradient mode)
+  void *C2;         // second output (SwiGLU: saved g|u; dW_up in weight-gradient mode)
+  long ldc2;
+  const uint16_t *aux;  // SwiGLU backward: saved g|u
+  long ldaux;
+  const float *bias;    // EPI_F32: optional per-column bias
+  const int32_t *offsets;     // [G+1] group row offsets
+  const int32_t *tile_start;  // [G+1] prefix of row tiles (row-ragged mode)
+  const int32_t *order;       // [G] group processing order (weight-gradient mode)
+  int G, M, N, K;
+  int n_tiles_m, n_tiles_n;
+};
+
+// Row-ragged grouped GEMM: for group g, rows [offsets[g], offsets[g+1]) of A
+// (K-contiguous, [rows][K]) times B_g (K-contiguous [N][K], or N-contiguous
+// [K][N] when b_kcontig is false) -> epilogue.  `max_rows` bounds the total
+// number of rows (sizes the grid).
+void launch_gemm_rows(const GemmArgs &p, int epi, bool b_kcontig, int max_rows, hipStream_t s);
+
+// Weight-gradient grouped GEMM: for group g, C_g[M][N] = sum over rows
+// [offsets[g], offsets[g+1]) of A[row][M]^T B[row][N] (both row-major with the
+// summed rows outermost).
+void launch_gemm_wgrad(const GemmArgs &p, int epi, hipStream_t s);
+
+}  // namespace moe

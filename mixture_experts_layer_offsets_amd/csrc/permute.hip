@@ -1,0 +1,390 @@
+// Data movement of the layer: dispatch, combine and their backward mirrors,
+// plus the router's weight gradient and weight packing.
+//
+// Sources: kucoin.com news flash "O MoK do Cursor alcança aumento de
+// desempenho de 2,37x no NVIDIA GB300 NVL72":
+//   §01  dispatch sends each token to its experts, combine returns every
+//        result to the token's original position; training adds two rounds
+//        in the opposite direction;
+//   §02  the destination pulls the rows it needs knowing only where each
+//        sits in the source (pull dispatch), results are pushed back to their
+//        known origin (push combine); the backward uses pull reverse-combine
+//        and push reverse-dispatch; MXFP8 activation quantisation is fused
+//        into dispatch;
+//   §03  the measured layer ends with the final weighted fusion.
+// On one GPU the "exchange" is an HBM gather or scatter: every kernel here
+// moves whole rows with 16-byte accesses, reads each source row once per use
+// and reduces in a fixed order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// MXFP8 block conversion (E4M3 elements, E8M0 scale per 32 values):
+//   s = clamp(floor(log2 amax) - 8, -127, 127), scale code s + 127
+//   code_i = E4M3(clamp(v_i * 2^-s, -448, 448)), nearest-even;
+//   an all-zero block gets scale code 0.
+
+__device__ __forceinline__ uint32_t e4m3_encode(float v, bool neg) {
+  const float a = fabsf(v);
+  const uint32_t sign = neg ? 0x80u : 0u;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // spacing 2^-9
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // round to 3 mantissa bits
+  const int e = (int)(r >> 23) - 127;
+  return sign | ((uint32_t)(e + 7) << 3) | ((r >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t ex = (c >> 3) & 15u, m = c & 7u;
+  const float mag = ex ? ldexpf((float)(8u + m), (int)ex - 10) : ldexpf((float)m, -9);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ int floor_log2(float a) {  // a > 0
+  const uint32_t u = __float_as_uint(a);
+  const int ex = (int)(u >> 23);
+  if (ex) return ex - 127;
+  return -149 + (31 - __clz(u & 0x7FFFFFu));
+}
+
+// Quantise 32 values; writes 32 codes (two uint4) and returns the scale code.
+// `deq` receives the dequantised values (may be null).
+__device__ __forceinline__ uint32_t mx_block(const float *v, uint4 *codes, float *deq) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+  int s = -127;
+  if (amax > 0.0f) {
+    s = floor_log2(amax) - 8;
+    s = s < -127 ? -127 : (s > 127 ? 127 : s);
+  }
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const float x = v[q * 4 + b];
+      const float sc = fminf(fmaxf(ldexpf(x, -s), -448.0f), 448.0f);
+      const uint32_t c = amax > 0.0f ? e4m3_encode(sc, x < 0.0f) : 0u;
+      d |= c << (8 * b);
+      if (deq) deq[q * 4 + b] = ldexpf(e4m3_value(c), s);
+    }
+    w[q] = d;
+  }
+  codes[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  codes[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  return (uint32_t)(s + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch.  One wave per sorted row r copies token perm[r] / k.
+
+__global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint4 *__restrict__ x,
+                                                            const int32_t *__restrict__ perm,
+                                                            uint4 *__restrict__ xp, int R, int k,
+                                                            int HC) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const uint4 *src = x + (size_t)(perm[r] / k) * HC;
+  uint4 *dst = xp + (size_t)r * HC;
+  for (int c = threadIdx.x & 63; c < HC; c += 64) dst[c] = src[c];
+}
+
+void launch_dispatch_bf16(const uint16_t *x, const int32_t *perm, uint16_t *xp, int R, int k,
+                          int H, hipStream_t s) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(dispatch_bf16_kernel, dim3((R + 3) / 4), dim3(256), 0, s,
+                     (const uint4 *)x, perm, (uint4 *)xp, R, k, H / 8);
+}
+
+// MX dispatch: one thread per 32-element block of a row.  Writes the E4M3
+// codes, the E8M0 scales and (if xhat) the dequantised row as bf16.
+__global__ __launch_bounds__(256) void dispatch_mx_kernel(
+    const uint4 *__restrict__ x, const int32_t *__restrict__ perm, uint4 *__restrict__ xq,
+    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int R, int k, int NB /* H/32 */) {
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long)R * NB) return;
+  const int r = (int)(id / NB), b = (int)(id - (long)r * NB);
+  const int src_row = perm ? perm[r] / k : r;
+  const uint4 *src = x + (size_t)src_row * NB * 4 + b * 4;
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; q++) unpack8(src[q], v + 8 * q);
+  uint4 codes[2];
+  float deq[32];
+  const uint32_t sc = mx_block(v, codes, xhat ? deq : nullptr);
+  uint4 *dq = xq + (size_t)r * NB * 2 + b * 2;
+  dq[0] = codes[0];
+  dq[1] = codes[1];
+  xs[(size_t)r * NB + b] = (uint8_t)sc;
+  if (xhat) {
+    uint4 *dh = xhat + (size_t)r * NB * 4 + b * 4;
+#pragma unroll
+    for (int q = 0; q < 4; q++) dh[q] = pack8(deq + 8 * q);
+  }
+}
+
+void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
+                        uint16_t *xhat, int R, int k, int H, hipStream_t s) {
+  const long n = (long)R * (H / 32);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const uint4 *)x, perm, (uint4 *)xq, xs, (uint4 *)xhat, R, k, H / 32);
+}
+
+// Row-wise MX quantisation of a bf16 matrix along its contiguous axis.
+void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
+                          hipStream_t s) {
+  const long n = (long)rows * (cols / 32);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const uint4 *)src, (const int32_t *)nullptr, (uint4 *)q, sc,
+                     (uint4 *)nullptr, rows, 1, cols / 32);
+}
+
+// ---------------------------------------------------------------------------
+// Combine + final weighted fusion: out[t] = sum_j w[t,j] y[inv[t*k+j]] (+ ys[t]),
+// fp32 fused multiply-adds in ascending j.  Grid (chunk groups, T).
+
+__global__ __launch_bounds__(128) void combine_kernel(const uint4 *__restrict__ y,
+                                                      const float *__restrict__ w,
+                                                      const int32_t *__restrict__ inv,
+                                                      const uint4 *__restrict__ ys,
+                                                      uint4 *__restrict__ out, int k, int HC) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 128 + threadIdx.x;
+  if (c >= HC) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; j++) {
+    const int f = t * k + j;
+    const float wj = w[f];
+    float v[8];
+    unpack8(y[(size_t)inv[f] * HC + c], v);
+#pragma unroll
+    for (int q = 0; q < 8; q++) acc[q] = fmaf(wj, v[q], acc[q]);
+  }
+  if (ys) {
+    float v[8];
+    unpack8(ys[(size_t)t * HC + c], v);
+#pragma unroll
+    for (int q = 0; q < 8; q++) acc[q] += v[q];
+  }
+  out[(size_t)t * HC + c] = pack8(acc);
+}
+
+void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,
+                    uint16_t *out, int T, int k, int H, hipStream_t s) {
+  const int HC = H / 8;
+  if (T <= 0) return;
+  hipLaunchKernelGGL(combine_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
+                     (const uint4 *)y, w, inv, (const uint4 *)ys, (uint4 *)out, k, HC);
+}
+
+// ---------------------------------------------------------------------------
+// Reverse-combine: each token's output gradient goes to its k rows scaled by
+// the slot weight, and dw[t,j] = <dout[t], y[row]>.  With a router, also the
+// selected-logit gradient dsel[t,j] = w_j (dw_j - sum_j' w_j' dw_j').
+// One 256-thread block per token; the dot products reduce in a fixed tree.
+
+constexpr int kMaxTopK = 16;
+
+__global__ __launch_bounds__(256) void reverse_combine_kernel(
+    const uint4 *__restrict__ dout, const uint4 *__restrict__ y, const float *__restrict__ w,
+    const int32_t *__restrict__ inv, uint4 *__restrict__ dy, float *__restrict__ dw,
+    float *__restrict__ dsel, int k, int HC) {
+  __shared__ float red[kMaxTopK][4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  float part[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; j++) part[j] = 0.0f;
+  int rows[kMaxTopK];
+  float wt[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; j++) {
+    rows[j] = j < k ? inv[t * k + j] : 0;
+    wt[j] = j < k ? w[t * k + j] : 0.0f;
+  }
+  for (int c = tid; c < HC; c += 256) {
+    float d[8];
+    unpack8(dout[(size_t)t * HC + c], d);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; j++) {
+      if (j < k) {
+        float v[8], o[8];
+        unpack8(y[(size_t)rows[j] * HC + c], v);
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          s = fmaf(d[q], v[q], s);
+          o[q] = wt[j] * d[q];
+        }
+        part[j] += s;
+        dy[(size_t)rows[j] * HC + c] = pack8(o);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; j++) {
+    if (j < k) {
+      const float s = wave_sum(part[j]);
+      if ((tid & 63) == 0) red[j][tid >> 6] = s;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const float dwj = tid < k ? (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]) : 0.0f;
+    if (tid < k && dw) dw[t * k + tid] = dwj;
+    if (dsel) {
+      const float wj = tid < k ? w[t * k + tid] : 0.0f;
+      const float sum = wave_sum(wj * dwj);
+      if (tid < k) dsel[t * k + tid] = wj * (dwj - sum);
+    }
+  }
+}
+
+void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float *w,
+                            const int32_t *inv, uint16_t *dy, float *dw, float *dsel, int T,
+                            int k, int H, hipStream_t s) {
+  if (T <= 0) return;
+  hipLaunchKernelGGL(reverse_combine_kernel, dim3(T), dim3(256), 0, s, (const uint4 *)dout,
+                     (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k, H / 8);
+}
+
+// ---------------------------------------------------------------------------
+// Reverse-dispatch: dx[t] = sum_j dX[inv[t*k+j]] + sum_j dsel[t,j] Wr^T[idx[t,j]]
+// (+ dxs[t]), fp32 in ascending j, stored as bf16.
+
+__global__ __launch_bounds__(128) void reverse_dispatch_kernel(
+    const uint4 *__restrict__ dX, const int32_t *__restrict__ inv, const int32_t *__restrict__ idx,
+    const float *__restrict__ dsel, const uint4 *__restrict__ wrT, const uint4 *__restrict__ dxs,
+    uint4 *__restrict__ dx, int k, int HC) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 128 + threadIdx.x;
+  if (c >= HC) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; j++) {
+    float v[8];
+    unpack8(dX[(size_t)inv[t * k + j] * HC + c], v);
+#pragma unroll
+    for (int q = 0; q < 8; q++) acc[q] += v[q];
+  }
+  if (wrT) {
+    for (int j = 0; j < k; j++) {
+      const float sj = dsel[t * k + j];
+      float v[8];
+      unpack8(wrT[(size_t)idx[t * k + j] * HC + c], v);
+#pragma unroll
+      for (int q = 0; q < 8; q++) acc[q] = fmaf(sj, v[q], acc[q]);
+    }
+  }
+  if (dxs) {
+    float v[8];
+    unpack8(dxs[(size_t)t * HC + c], v);
+#pragma unroll
+    for (int q = 0; q < 8; q++) acc[q] += v[q];
+  }
+  dx[(size_t)t * HC + c] = pack8(acc);
+}
+
+void launch_reverse_dispatch(const uint16_t *dX, const int32_t *inv, const int32_t *idx,
+                             const float *dsel, const uint16_t *wrT, const uint16_t *dxs,
+                             uint16_t *dx, int T, int k, int H, hipStream_t s) {
+  const int HC = H / 8;
+  if (T <= 0) return;
+  hipLaunchKernelGGL(reverse_dispatch_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
+                     (const uint4 *)dX, inv, idx, dsel, (const uint4 *)wrT, (const uint4 *)dxs,
+                     (uint4 *)dx, k, HC);
+}
+
+// ---------------------------------------------------------------------------
+// Router weight gradient: dWr[h][e] = sum over expert e's rows of
+// dsel[f] * x[f/k][h], rows in sorted (ascending) order.  Grid (H/2048, E).
+
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const uint4 *__restrict__ x,
+                                                           const int32_t *__restrict__ perm,
+                                                           const int32_t *__restrict__ offsets,
+                                                           const float *__restrict__ dsel,
+                                                           float *__restrict__ dwr, int E, int k,
+                                                           int HC) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= HC) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int r1 = offsets[e + 1];
+  for (int r = offsets[e]; r < r1; r++) {
+    const int f = perm[r];
+    const float s = dsel[f];
+    float v[8];
+    unpack8(x[(size_t)(f / k) * HC + c], v);
+#pragma unroll
+    for (int q = 0; q < 8; q++) acc[q] = fmaf(s, v[q], acc[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; q++) dwr[(size_t)(c * 8 + q) * E + e] = acc[q];
+}
+
+void launch_router_wgrad(const uint16_t *x, const int32_t *perm, const int32_t *offsets,
+                         const float *dsel, float *dwr, int E, int k, int H, hipStream_t s) {
+  const int HC = H / 8;
+  hipLaunchKernelGGL(router_wgrad_kernel, dim3((HC + 255) / 256, E), dim3(256), 0, s,
+                     (const uint4 *)x, perm, offsets, dsel, dwr, E, k, HC);
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing.
+// transpose_pack: out[g][map(c)][r] = in[g][r][c] for in [G][rows][cols],
+//   map(c) = (c / 32) * blk_stride + blk_off + c % 32; out rows have `rows`
+//   elements; out has out_rows_total rows per group.
+// interleave_copy: out[g][r][map(c)] = in[g][r][c]; out rows have out_cols.
+
+__global__ __launch_bounds__(256) void transpose_pack_kernel(const uint16_t *__restrict__ in,
+                                                             uint16_t *__restrict__ out, int rows,
+                                                             int cols, int out_rows_total,
+                                                             int blk_stride, int blk_off) {
+  __shared__ uint16_t tile[64][65];
+  const int g = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t *src = in + (size_t)g * rows * cols;
+  uint16_t *dst = out + (size_t)g * out_rows_total * rows;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i >> 6, cc = i & 63;
+    if (r0 + rr < rows && c0 + cc < cols) tile[rr][cc] = src[(size_t)(r0 + rr) * cols + c0 + cc];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i >> 6, rr = i & 63;
+    const int c = c0 + cc, r = r0 + rr;
+    if (r < rows && c < cols) {
+      const int orow = (c >> 5) * blk_stride + blk_off + (c & 31);
+      dst[(size_t)orow * rows + r] = tile[rr][cc];
+    }
+  }
+}
+
+void launch_transpose_pack(const uint16_t *in, uint16_t *out, int G, int rows, int cols,
+                           int out_rows_total, int blk_stride, int blk_off, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_pack_kernel, dim3((cols + 63) / 64, (rows + 63) / 64, G),
+                     dim3(256), 0, s, in, out, rows, cols, out_rows_total, blk_stride, blk_off);
+}
+
+__global__ __launch_bounds__(256) void interleave_copy_kernel(const uint16_t *__restrict__ in,
+                                                              uint16_t *__restrict__ out,
+                                                              int rows, int cols, int out_cols,
+                                                              int blk_stride, int blk_off) {
+  const int g = blockIdx.z, r = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int oc = (c >> 5) * blk_stride + blk_off + (c & 31);
+  out[((size_t)g * rows + r) * out_cols + oc] = in[((size_t)g * rows + r) * cols + c];
+}
+
+void launch_interleave_copy(const uint16_t *in, uint16_t *out, int G, int rows, int cols,
+                            int out_cols, int blk_stride, int blk_off, hipStream_t s) {
+  hipLaunchKernelGGL(interleave_copy_kernel, dim3((cols + 255) / 256, rows, G), dim3(256), 0, s,
+                     in, out, rows, cols, out_cols, blk_stride, blk_off);
+}
+
+}  // namespace moe

@@ -1,0 +1,125 @@
+"""The C ABI: libmoe.so loads and exports every entry point include/moe.h
+declares, the binding covers exactly those, and host-side checks (sizes,
+argument validation) behave as documented.  No test here launches a kernel:
+every validation case returns before the library touches the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_offsets_amd as m
+from mixture_experts_layer_offsets_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_layer_offsets_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def test_header_declares_the_layer_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_layout", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+              "moe_layer_fwd", "moe_layer_bwd", "moe_workspace_bytes", "moe_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+
+
+def declared_arity():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(moe_\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    ar = declared_arity()
+    assert set(ar) == set(_lib.SIGNATURES)
+    for n, (_, args) in _lib.SIGNATURES.items():
+        assert len(args) == ar[n], (n, len(args), ar[n])
+
+
+def test_struct_layouts_match_header():
+    text = open(HEADER).read()
+    for cname, pyt in (("moe_shape", _lib.MoeShape), ("moe_sched", _lib.MoeSched),
+                       ("moe_saved_view", _lib.MoeSavedView)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (cname, cname), text, re.S).group(1)
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        fields = re.findall(r"(\w+)\s*;", body)
+        assert fields == [f for f, _ in pyt._fields_], cname
+
+
+def test_sizes(lib):
+    kimi = m.Shape(2048, 7168, 6, 8, 2048)
+    ws, sv, pk = (m.moe_workspace_bytes(kimi), m.moe_saved_bytes(kimi),
+                  m.moe_packed_weight_bytes(kimi))
+    R, H, I, E = 2048 * 8, 7168, 2048, 6
+    assert sv >= R * H * 2 * 2 + R * 3 * I * 2       # x_perm, y, g|u, a
+    assert ws >= R * H * 2 * 2 + R * 2 * I * 2       # dY, dX, dh
+    assert pk >= 4 * 3 * E * H * I // 2 * 2          # four bf16 copies of 3 E H I / 2 ... lower bound
+    for v in (ws, sv, pk):
+        assert v % 256 == 0
+    bad = m.Shape(0, 7168, 6, 8, 2048)
+    assert m.moe_workspace_bytes(bad) == 0
+    assert m.moe_saved_bytes(m.Shape(16, 100, 4, 2, 64)) == 0      # H not a multiple of 64
+    assert m.moe_packed_weight_bytes(m.Shape(16, 64, 2000, 2, 64)) == 0  # E > 1024
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def test_argument_validation_returns_codes(lib):
+    s = ctypes.byref(m.Shape(64, 128, 8, 2, 64).c())
+    # NULL required pointers
+    assert lib.moe_route(s, None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(s, None, None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(s, None, None, None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_fwd(s, None, None, None, None, None, None, None, None, None, None, 0,
+                             None) == _lib.MOE_ERR_INVALID_ARG
+    # a workspace that is too small (pointer is never dereferenced on this path)
+    fake = 1 << 40
+    assert lib.moe_layout(s, fake, fake, fake, fake, fake, fake, 16, None) == \
+        _lib.MOE_ERR_WORKSPACE
+    # both a router and supplied routing
+    assert lib.moe_layer_fwd(s, None, fake, fake, None, fake, fake, fake, fake, fake, fake,
+                             1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    # k > E when routing from logits
+    s2 = ctypes.byref(m.Shape(64, 128, 4, 6, 64).c())
+    assert lib.moe_route(s2, fake, fake, fake, None) == _lib.MOE_ERR_INVALID_ARG
+    # shapes outside the kernels' limits
+    s3 = ctypes.byref(m.Shape(64, 96, 4, 2, 64).c())
+    assert lib.moe_route(s3, fake, fake, fake, None) == _lib.MOE_ERR_UNSUPPORTED
+    s4 = ctypes.byref(m.Shape(64, 128, 4, 17, 64).c())
+    assert lib.moe_layout(s4, fake, fake, fake, fake, fake, fake, 1 << 40, None) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(None, fake, fake, fake, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_strerror(lib):
+    assert m.moe_strerror(0) == "ok"
+    assert "workspace" in m.moe_strerror(_lib.MOE_ERR_WORKSPACE)
+    assert m.moe_strerror(12345) == "unknown error"
