@@ -39,9 +39,26 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="kimi-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=96,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the bounded oracle sample (CPU baseline)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain device-to-device copy of known size: what FETCH_SIZE/WRITE_SIZE
+    read for it calibrates the counters used for the layer's kernels."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n}), flush=True)
 
 
 def _algorithmic(w):
@@ -109,6 +126,9 @@ def cpu_baseline(w, inp, tokens: int):
 
 def main():
     a = _args()
+    if a.copy_probe:
+        copy_probe()
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {a.gpus}).", file=sys.stderr)
@@ -192,7 +212,7 @@ def main():
 
     dom = "gemm_gate_up_swiglu"
     achieved = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
-    traffic = _traffic("grouped_gemm_kernel<false, true, 2>")
+    traffic = _traffic("gemm_nt_kernel<2>")
     tokens_per_step = w.T
     res = {
         "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X" if w.backward
@@ -215,8 +235,8 @@ def main():
                                + (f", Zipf s={w.zipf_s}" if w.routing == "supplied" else ""),
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k,
                    "inter": w.I, "routed_rows": w.T * w.k},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<false, true, 2> "
-                     "(gate/up GEMM + SwiGLU epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel<2> "
+                     "(gate/up grouped GEMM + SwiGLU epilogue)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "avg_launch_ms": stage_ms[dom]},

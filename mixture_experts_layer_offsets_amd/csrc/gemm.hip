@@ -14,13 +14,18 @@
 //     heaviest first so the long tiles start early.
 //
 // Tile: 256 x 256 outputs per 256-thread workgroup, four waves of 128 x 128,
-// each wave a 4 x 4 grid of v_mfma_f32_32x32x16_bf16.  Operands are staged
-// through LDS in 64-deep K slices, double buffered (2 x 64 KB).  LDS rows hold
-// 64 bf16 of K in eight 16-byte chunks whose positions are XOR-swizzled by
-// the row, so both the global->LDS stores and the MFMA fragment reads are
-// free of bank conflicts.  Operands whose contiguous axis is M or N (the
-// weight gradients, the router) are loaded as 8x8 blocks and transposed in
-// registers on their way into the same LDS layout.
+// each wave a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs).
+// Operands are staged through LDS in 64-deep K slices, double buffered.
+//   * gemm_nt_kernel (both operands contraction-contiguous: the forward
+//     GEMMs and the backward data gradients) moves operands with
+//     buffer_load_dwordx4 ... lds straight into an XOR-swizzled LDS layout.
+//   * grouped_gemm_kernel (weight gradients and the router, where an operand
+//     is contiguous along M or N) loads 8x8 blocks into registers and
+//     transposes them on the way into the same LDS layout.
+// Measured on MI355X: the MFMA ceiling of this instruction with one wave per
+// SIMD is ~2.1 PFLOP/s, and a CU's L2->LDS feed tops out near 34 B/clk --
+// about what a 256 x 256 bf16 tile consumes at full MFMA rate -- so the
+// kernels are co-limited by operand feed and matrix issue.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,6 +54,83 @@ __device__ __forceinline__ void transpose8x8(const uint4 *in, uint4 *out) {
       d[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
     out[j] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Epilogue shared by both kernels.  acc[i][j][v] holds row
+// wm0 + 32i + 8(v/4) + 4(lane/32) + v%4 and column wn0 + 32j + lane%32 of the tile.
+template <bool WGRAD, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs &p, f32x16 (&acc)[4][4], int g, int m0,
+                                         int n0, int rowbase, int Mg, int wm0, int wn0,
+                                         int lane) {
+  const int N = p.N;
+  const int ncol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      const int m = m0 + wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (m >= Mg) continue;
+      if constexpr (EPI == EPI_BF16) {
+        uint16_t *C = (uint16_t *)p.C + (size_t)(rowbase + m) * p.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int n = n0 + wn0 + j * 32 + ncol;
+          if (n < N) C[n] = (uint16_t)f32_to_bf16(acc[i][j][v]);
+        }
+      } else if constexpr (EPI == EPI_F32) {
+        float *C = WGRAD ? (float *)p.C + (size_t)g * p.sC + (size_t)m * p.ldc
+                         : (float *)p.C + (size_t)(rowbase + m) * p.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int n = n0 + wn0 + j * 32 + ncol;
+          if (n < N) C[n] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.0f);
+        }
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        // packed columns: 64-column blocks of [32 gate | 32 up]
+        uint16_t *A = (uint16_t *)p.C + (size_t)(rowbase + m) * p.ldc;
+        uint16_t *GU = p.C2 ? (uint16_t *)p.C2 + (size_t)(rowbase + m) * p.ldc2 : nullptr;
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+          const int n = n0 + wn0 + jj * 64 + ncol;  // gate column
+          if (n < N) {
+            const float gv = acc[i][2 * jj][v], uv = acc[i][2 * jj + 1][v];
+            A[(n >> 6) * 32 + ncol] = (uint16_t)f32_to_bf16(silu_f(gv) * uv);
+            if (GU) {
+              GU[n] = (uint16_t)f32_to_bf16(gv);
+              GU[n + 32] = (uint16_t)f32_to_bf16(uv);
+            }
+          }
+        }
+      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        // columns are intermediate indices i; read g, u; write dg, du packed
+        const uint16_t *GU = p.aux + (size_t)(rowbase + m) * p.ldaux;
+        uint16_t *DH = (uint16_t *)p.C + (size_t)(rowbase + m) * p.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int n = n0 + wn0 + j * 32 + ncol;
+          if (n < N) {
+            const int pg = (n >> 5) * 64 + (n & 31);
+            const float gv = bf16_to_f32(GU[pg]), uv = bf16_to_f32(GU[pg + 32]);
+            const float dA = acc[i][j][v];
+            const float s = sigmoid_f(gv);
+            DH[pg] = (uint16_t)f32_to_bf16(dA * uv * s * (1.0f + gv * (1.0f - s)));
+            DH[pg + 32] = (uint16_t)f32_to_bf16(dA * gv * s);
+          }
+        }
+      } else if constexpr (EPI == EPI_WGRAD_GU) {
+        // rows h, packed columns -> dW_gate / dW_up [g][h][i]
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int n = n0 + wn0 + j * 32 + ncol;
+          if (n < N) {
+            const int ii = (n >> 6) * 32 + (n & 31);
+            float *D = (float *)(((n >> 5) & 1) ? p.C2 : p.C) + (size_t)g * p.sC;
+            D[(size_t)m * p.ldc + ii] = acc[i][j][v];
+          }
+        }
+      }
+    }
   }
 }
 
@@ -214,76 +296,141 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- epilogue.  acc[i][j][v] holds row wm0 + 32i + 8(v/4) + 4(lane/32) + v%4
-  // and column wn0 + 32j + lane%32 of the tile.
-  const int ncol = lane & 31;
+  epilogue<WGRAD, EPI>(p, acc, g, m0, n0, rowbase, Mg, wm0, wn0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Row-ragged GEMM with both operands contraction-contiguous (the forward
+// gate/up and down GEMMs and both backward data-gradient GEMMs).
+//
+// Operands move from HBM straight into LDS with buffer_load_dwordx4 ... lds:
+// no staging registers and no ds_write instructions.  A wave's 16-byte load
+// lands lane-linearly in a 1 KB LDS segment (8 rows of 128 bytes), so each
+// lane fetches the global chunk that the XOR swizzle assigns to its LDS slot.
+// The buffer descriptor covers exactly the tile's valid rows: rows past the
+// end of the group read as zeros, with no per-row masks.  Two LDS buffers
+// (separate arrays, so the compiler can tell the one being filled from the
+// one being read) alternate per 64-deep K slice; MFMA fragments are double
+// buffered in registers so LDS latency hides behind the previous 16 MFMAs.
+
+constexpr uint32_t kBufferDword3 = 0x00020000;  // raw buffer, gfx9 family
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Chunk swizzle of the DMA-fed tiles (rows of 64 bf16 = eight 16-byte
+// chunks).  It uses row bits 0..4 only: the rows read by any 8 (or 16)
+// consecutive lanes of an MFMA fragment land in distinct bank groups, and the
+// fragment addresses of the four 32-row blocks differ by immediates only.
+__device__ __forceinline__ int swz5(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t L0[2 * BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t L1[2 * BM * BK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int MT = p.tile_start[p.G];
+  const int nN = p.n_tiles_n;
+  const int total = MT * nN;
+  const int b = blockIdx.x;
+  if (b >= total) return;
+  // consecutive blocks share the A row tile (n fastest); measured faster on
+  // this chip than XCD-grouped rasters for these shapes
+  const int mt = b / nN, nt = b - (b / nN) * nN;
+  int lo = 0, hi = p.G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_start[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int m0 = (mt - p.tile_start[g]) * BM;
+  const int n0 = nt * BN;
+  const int rowbase = p.offsets[g];
+  const int Mg = p.offsets[g + 1] - rowbase;
+  const int a_rows = min(BM, Mg - m0), b_rows = min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.A + (size_t)(rowbase + m0) * p.lda), (short)0, a_rows * (int)p.lda * 2,
+      kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.B + (size_t)g * p.sB + (size_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb * 2,
+      kBufferDword3);
+  uint32_t oa[8], ob[8];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < 8; i++) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz5(row);
+    oa[i] = (uint32_t)(row * (int)p.lda * 2 + kc * 16);
+    ob[i] = (uint32_t)(row * (int)p.ldb * 2 + kc * 16);
+  }
+  auto issue = [&](uint16_t *L, int kt) {
+    const int soff = kt * BK * 2;
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int m = m0 + wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (m >= Mg) continue;
-      if constexpr (EPI == EPI_BF16) {
-        uint16_t *C = (uint16_t *)p.C + (size_t)(rowbase + m) * p.ldc;
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
+                                               oa[i], soff, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int n = n0 + wn0 + j * 32 + ncol;
-          if (n < N) C[n] = (uint16_t)f32_to_bf16(acc[i][j][v]);
-        }
-      } else if constexpr (EPI == EPI_F32) {
-        float *C = WGRAD ? (float *)p.C + (size_t)g * p.sC + (size_t)m * p.ldc
-                         : (float *)p.C + (size_t)(rowbase + m) * p.ldc;
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + BM * BK + (wave * 8 + i) * 512),
+                                               16, ob[i], soff, 0, 0);
+  };
+  f32x16 acc[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int n = n0 + wn0 + j * 32 + ncol;
-          if (n < N) C[n] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.0f);
-        }
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        // packed columns: 64-column blocks of [32 gate | 32 up]
-        uint16_t *A = (uint16_t *)p.C + (size_t)(rowbase + m) * p.ldc;
-        uint16_t *GU = p.C2 ? (uint16_t *)p.C2 + (size_t)(rowbase + m) * p.ldc2 : nullptr;
+  for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int jj = 0; jj < 2; jj++) {
-          const int n = n0 + wn0 + jj * 64 + ncol;  // gate column
-          if (n < N) {
-            const float gv = acc[i][2 * jj][v], uv = acc[i][2 * jj + 1][v];
-            A[(n >> 6) * 32 + ncol] = (uint16_t)f32_to_bf16(silu_f(gv) * uv);
-            if (GU) {
-              GU[n] = (uint16_t)f32_to_bf16(gv);
-              GU[n + 32] = (uint16_t)f32_to_bf16(uv);
-            }
-          }
-        }
-      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        // columns are intermediate indices i; read g, u; write dg, du packed
-        const uint16_t *GU = p.aux + (size_t)(rowbase + m) * p.ldaux;
-        uint16_t *DH = (uint16_t *)p.C + (size_t)(rowbase + m) * p.ldc;
+    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+  const int fr = lane & 31;
+  const int cA = swz5(fr) ^ (lane >> 5);
+  const int baseA = (wm0 + fr) * BK, baseB = BM * BK + (wn0 + fr) * BK;
+  int offk[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int n = n0 + wn0 + j * 32 + ncol;
-          if (n < N) {
-            const int pg = (n >> 5) * 64 + (n & 31);
-            const float gv = bf16_to_f32(GU[pg]), uv = bf16_to_f32(GU[pg + 32]);
-            const float dA = acc[i][j][v];
-            const float s = sigmoid_f(gv);
-            DH[pg] = (uint16_t)f32_to_bf16(dA * uv * s * (1.0f + gv * (1.0f - s)));
-            DH[pg + 32] = (uint16_t)f32_to_bf16(dA * gv * s);
-          }
-        }
-      } else if constexpr (EPI == EPI_WGRAD_GU) {
-        // rows h, packed columns -> dW_gate / dW_up [g][h][i]
+  for (int ks = 0; ks < 4; ks++) offk[ks] = ((2 * ks) ^ cA) << 3;
+  auto compute = [&](const uint16_t *L) {
+    bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int n = n0 + wn0 + j * 32 + ncol;
-          if (n < N) {
-            const int ii = (n >> 6) * 32 + (n & 31);
-            float *D = (float *)(((n >> 5) & 1) ? p.C2 : p.C) + (size_t)g * p.sC;
-            D[(size_t)m * p.ldc + ii] = acc[i][j][v];
-          }
+    for (int i = 0; i < 4; i++) {
+      fa[0][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[0]);
+      fb[0][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[0]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++) {
+      const int c = ks & 1, nx = c ^ 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          fa[nx][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[ks + 1]);
+          fb[nx][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[ks + 1]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0,
+                                                              0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  const int nk = p.K / BK;
+  issue(L0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    issue(L1, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(L0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) issue(L0, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(L1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
+  if (kt < nk) compute(L0);
+  epilogue<false, EPI>(p, acc, g, m0, n0, rowbase, Mg, wm0, wn0, lane);
 }
 
 template <bool WGRAD, bool B_KC>
@@ -304,6 +451,16 @@ void launch_gemm_rows(const GemmArgs &p0, int epi, bool b_kcontig, int max_rows,
   const long m_tiles = (long)max_rows / BM + p.G;
   const long grid = m_tiles * p.n_tiles_n;
   if (grid <= 0) return;
+  if (b_kcontig && p.K % BK == 0 &&
+      (epi == EPI_BF16 || epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD)) {
+    const dim3 gr((unsigned)grid), b(NT);
+    switch (epi) {
+      case EPI_BF16: hipLaunchKernelGGL(gemm_nt_kernel<EPI_BF16>, gr, b, 0, s, p); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL(gemm_nt_kernel<EPI_SWIGLU>, gr, b, 0, s, p); break;
+      default: hipLaunchKernelGGL(gemm_nt_kernel<EPI_SWIGLU_BWD>, gr, b, 0, s, p); break;
+    }
+    return;
+  }
   if (b_kcontig) launch_epi<false, true>(p, epi, (int)grid, s);
   else launch_epi<false, false>(p, epi, (int)grid, s);
 }
