@@ -360,6 +360,30 @@ def router_backward(x, w_router, idx, w, dw, E, exact=False):
 # Brute force per token: no layout, no permutation
 
 
+class _LazyWeights:
+    """Per-expert decoded weights (as the forward / backward GEMMs see them),
+    decoded on first use: the sampled evaluators touch only a few experts."""
+
+    def __init__(self, inp, mx, shared=False, keep=16):
+        if shared:
+            self.src = (inp["ws_gate"][None], inp["ws_up"][None], inp["ws_down"][None])
+        else:
+            self.src = (inp["w_gate"], inp["w_up"], inp["w_down"])
+        self.mx = mx
+        self.keep = keep
+        self.cache = {}
+
+    def __getitem__(self, e):
+        if e in self.cache:
+            self.cache[e] = self.cache.pop(e)          # most recently used last
+        else:
+            if len(self.cache) >= self.keep:
+                self.cache.pop(next(iter(self.cache)))
+            one = dict(w_gate=self.src[0][e], w_up=self.src[1][e], w_down=self.src[2][e])
+            self.cache[e] = _weights(one, self.mx)
+        return self.cache[e]
+
+
 class TokenEvaluator:
     """Evaluate chosen tokens' outputs and gradients one token at a time.
 
@@ -374,8 +398,9 @@ class TokenEvaluator:
         self.inp, self.k, self.mx = inp, k, mx
         self.R = _Round(False)
         self.x = _val(inp["x"])
-        self.W = _weights(inp, mx)
-        self.WS = _shared_weights(inp, mx)
+        self.W = _LazyWeights(inp, mx)
+        self.WS = _LazyWeights(inp, mx, shared=True)[0] if inp.get("ws_gate") is not None \
+            else None
         if inp.get("topk_idx") is None:
             self.routing = None
         else:
@@ -393,15 +418,15 @@ class TokenEvaluator:
         return mx_roundtrip(xt, axis=1) if self.mx else xt
 
     def token(self, t):
-        """Forward of token t: dict(idx, w, rows=[per-slot g,u,ahat,Y], ys, out)."""
+        """Forward of token t: dict(idx, w, slots=[per-slot g,u,ahat,Y], shared, out)."""
         idx, w = self.route(t)
         xh = self._xhat(t)
         slots = []
         acc = np.zeros(self.x.shape[1])
         for j in range(self.k):
             e = int(idx[j])
-            g, u, ah, Y = _swiglu_rows(xh, self.W["g"][e], self.W["u"][e], self.W["d"][e],
-                                       self.mx, self.R)
+            We = self.W[e]
+            g, u, ah, Y = _swiglu_rows(xh, We["g"], We["u"], We["d"], self.mx, self.R)
             slots.append(dict(e=e, g=g, u=u, ahat=ah, Y=Y[0]))
             acc += w[j] * Y[0]
         ys = None
@@ -418,13 +443,12 @@ class TokenEvaluator:
         dw = self.R.f32(np.array([dout_t @ s["Y"] for s in fw["slots"]]))
         acc = np.zeros_like(dout_t)
         for j, s in enumerate(fw["slots"]):
-            e = s["e"]
+            We = self.W[s["e"]]
             dY = self.R.bf16(w[j] * dout_t)[None, :]
-            Wb = dict(d_b=self.W["d_b"][e], g_b=self.W["g_b"][e], u_b=self.W["u_b"][e])
-            b = _swiglu_rows_bwd(fw["xhat"], s["g"], s["u"], s["ahat"], dY, Wb, self.mx, self.R)
+            b = _swiglu_rows_bwd(fw["xhat"], s["g"], s["u"], s["ahat"], dY, We, self.mx, self.R)
             acc += b["dX"][0]
         if self.routing is None:
-            E = self.W["g"].shape[0]
+            E = self.inp["w_gate"].shape[0]
             _, _, _, dxr = router_backward(self.x[t:t + 1], self.inp["w_router"],
                                            fw["idx"][None], w[None], dw[None], E)
             acc += dxr[0]
@@ -436,38 +460,45 @@ class TokenEvaluator:
         return dict(dw=dw, dx=self.R.bf16(acc))
 
 
-def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None):
+def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False):
     """dW_down[e, i, :], dW_gate[e, :, i], dW_up[e, :, i] for chosen columns i.
 
     Sums over the rows routed to expert e (found from the routing by
     :func:`layout`), recomputing only the 32-column blocks of g, u, a and dA
     that the chosen columns fall in.  For sampled checks at full size.
     Router routing is evaluated in full (it is cheap); the FFN is not.
+    With ``shared`` the expert is the shared one: every token, weight one.
     """
     R = _Round(False)
     x = _val(inp["x"])
     dout = _val(inp["dout"] if dout is None else dout)
-    W = _weights(inp, mx)
-    if inp.get("topk_idx") is None:
-        L = router_logits(x, inp["w_router"], inp.get("bias"))
-        idx, w = topk_softmax(L, k)
+    if shared:
+        We = _LazyWeights(inp, mx, shared=True)[0]
+        t = np.arange(x.shape[0])
+        wrow = np.ones(x.shape[0])
     else:
-        idx, w = np.asarray(inp["topk_idx"]), _val(inp["topk_w"])
-    E = W["g"].shape[0]
-    _, offsets, perm, _ = layout(idx, E)
-    f = perm[offsets[e]:offsets[e + 1]].astype(np.int64)
-    t = f // k
+        We = _LazyWeights(inp, mx)[e]
+        if inp.get("topk_idx") is None:
+            L = router_logits(x, inp["w_router"], inp.get("bias"))
+            idx, w = topk_softmax(L, k)
+        else:
+            idx, w = np.asarray(inp["topk_idx"]), _val(inp["topk_w"])
+        E = inp["w_gate"].shape[0]
+        _, offsets, perm, _ = layout(idx, E)
+        f = perm[offsets[e]:offsets[e + 1]].astype(np.int64)
+        t = f // k
+        wrow = np.asarray(w, np.float64).reshape(-1)[f]
     xh = mx_roundtrip(x[t], axis=1) if mx else x[t]
-    dY = R.bf16(np.asarray(w, np.float64).reshape(-1)[f][:, None] * dout[t])
+    dY = R.bf16(wrow[:, None] * dout[t])
     cols = np.asarray(cols)
     blocks = np.unique(cols // 32)
     bc = np.concatenate([np.arange(b * 32, b * 32 + 32) for b in blocks])
-    g = R.f32(xh @ W["g"][e][:, bc])
-    u = R.f32(xh @ W["u"][e][:, bc])
+    g = R.f32(xh @ We["g"][:, bc])
+    u = R.f32(xh @ We["u"][:, bc])
     a = silu(g) * u
     ah = mx_roundtrip(a, axis=1) if mx else R.bf16(a)
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
-    dA = R.f32(dYq @ W["d_b"][e][bc, :].T)
+    dA = R.f32(dYq @ We["d_b"][bc, :].T)
     s = sigmoid(g)
     dg = R.bf16(dA * u * s * (1.0 + g * (1.0 - s)))
     du = R.bf16(dA * g * s)
@@ -476,4 +507,4 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None):
         dWd=R.f32(ah[:, pos].T @ dY),          # [len(cols), H]
         dWg=R.f32(xh.T @ dg[:, pos]).T,        # [len(cols), H]
         dWu=R.f32(xh.T @ du[:, pos]).T,        # [len(cols), H]
-        rows=int(f.size))
+        rows=int(t.size))

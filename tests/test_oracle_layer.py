@@ -238,3 +238,32 @@ def test_mx_mode_close_to_bf16_mode():
     for n in ("dx", "dWg", "dWu", "dWd"):
         rel = np.abs(ga[n] - gb[n]).max() / np.abs(ga[n]).max()
         assert 0 < rel < 0.15, n
+
+
+@pytest.mark.parametrize("name", ["router", "supplied-dup", "router-mx"])
+def test_sampled_weight_gradient_columns_match_full_backward(name):
+    from oracle.layer import expert_weight_grad_columns
+    w = CASES[name]
+    inp = synth.make_inputs(w)
+    fw = oracle.forward(inp, w.k, mx=w.mx)
+    bw = oracle.backward(inp, fw)
+    for e in range(w.E):
+        cols = np.array([0, 5, w.I - 1])
+        got = expert_weight_grad_columns(inp, w.k, w.mx, e, cols)
+        assert np.array_equal(got["dWd"], bw["dWd"][e][cols, :])
+        assert np.array_equal(got["dWg"], bw["dWg"][e][:, cols].T)
+        assert np.array_equal(got["dWu"], bw["dWu"][e][:, cols].T)
+        assert got["rows"] == fw["counts"][e]
+
+
+def test_sampled_shared_expert_columns_match_full_backward():
+    from oracle.layer import expert_weight_grad_columns
+    w = CASES["shared"]
+    inp = synth.make_inputs(w)
+    fw = oracle.forward(inp, w.k)
+    bw = oracle.backward(inp, fw)
+    cols = np.array([1, 33, w.shared_I - 1])
+    got = expert_weight_grad_columns(inp, w.k, False, 0, cols, shared=True)
+    assert np.array_equal(got["dWd"], bw["dWsd"][cols, :])
+    assert np.array_equal(got["dWg"], bw["dWsg"][:, cols].T)
+    assert np.array_equal(got["dWu"], bw["dWsu"][:, cols].T)
