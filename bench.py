@@ -23,7 +23,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (the MX-scaled fp8 instruction)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+# GEMM stages whose operands are MXFP8 when the layer runs in MXFP8 (the
+# weight gradients stay bf16)
+MX_GEMMS = ("gemm_gate_up_swiglu", "gemm_down", "gemm_dgrad_down_swiglu_bwd",
+            "gemm_dgrad_gate_up")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_offsets_amd", "csrc")
+KERNEL_SOURCES = {
+    "gemm_nt_kernel<2>": ("gemm.hip", "gemm_common.h"),
+    "gemm_mx_kernel<2>": ("gemm_mx.hip", "gemm_common.h", "mx_device.h"),
+}
 
 FWD_STAGES = ["route+layout", "dispatch", "gemm_gate_up_swiglu", "gemm_down", "shared",
               "combine"]
@@ -72,9 +83,12 @@ def _algorithmic(w):
         "gemm_dgrad_gate_up": 4.0 * R * H * I,
         "gemm_wgrad_gate_up": 4.0 * R * H * I,
     }
+    # bytes per element of a dispatched row: bf16, or an E4M3 code plus a
+    # 1/32 share of an E8M0 scale
+    xb = 1.0 + 1.0 / 32 if w.mx else 2.0
     b = {
         # unique token rows read once, routed rows written once, + indices
-        "dispatch": T * H * 2 + R * H * 2 + R * 4,
+        "dispatch": T * H * 2 + R * H * xb + R * 4,
         # routed rows read once, token rows written once, + weights/indices
         "combine": R * H * 2 + T * H * 2 + R * 8,
         # dOut read once, Y read for dw, dY written, + weights/indices/dw
@@ -83,18 +97,23 @@ def _algorithmic(w):
     return f, b
 
 
-def _traffic(kernel: str):
+def sources_sha256(kernel: str) -> str:
+    """Hash of the source files a kernel is built from."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def _traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on this workload and the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path))
-        src = os.path.join(ROOT, "mixture_experts_layer_offsets_amd", "csrc", "gemm.hip")
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        ent = rec.get(kernel)
-        if not ent or ent.get("gemm_hip_sha256") != sha:
+        ent = json.load(open(path)).get(f"{kernel} {workload}")
+        if not ent or ent.get("sources_sha256") != sources_sha256(kernel):
             return None
         return ent["bytes_per_launch"]
     except Exception:
@@ -205,14 +224,18 @@ def main():
         for i, name in enumerate(BWD_STAGES):
             stage_ms[name] = float(np.mean([b[i].elapsed_time(b[i + 1]) for _, b in ev]))
     flops, byts = _algorithmic(w)
-    mfma = {k: flops[k] / (stage_ms[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+
+    def peak(stage):
+        return PEAK_FP8_TFLOPS if w.mx and stage in MX_GEMMS else PEAK_BF16_TFLOPS
+    mfma = {k: flops[k] / (stage_ms[k] * 1e-3) / 1e12 / peak(k)
             for k in flops if k in stage_ms and stage_ms[k] > 0}
     hbm = {k: byts[k] / (stage_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS
            for k in byts if k in stage_ms and stage_ms[k] > 0}
 
     dom = "gemm_gate_up_swiglu"
     achieved = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
-    traffic = _traffic("gemm_nt_kernel<2>")
+    kernel = "gemm_mx_kernel<2>" if w.mx else "gemm_nt_kernel<2>"
+    traffic = _traffic(kernel, w.name)
     tokens_per_step = w.T
     res = {
         "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X" if w.backward
@@ -235,10 +258,10 @@ def main():
                                + (f", Zipf s={w.zipf_s}" if w.routing == "supplied" else ""),
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k,
                    "inter": w.I, "routed_rows": w.T * w.k},
-        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel<2> "
+        "roofline": {"bound": "mfma", "kernel": f"{kernel} "
                      "(gate/up grouped GEMM + SwiGLU epilogue)",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "achieved": achieved, "peak": peak(dom), "unit": "TFLOP/s",
+                     "frac": achieved / peak(dom), "traffic": traffic,
                      "avg_launch_ms": stage_ms[dom]},
         "stage_ms": stage_ms,
         "mfma_frac": mfma,

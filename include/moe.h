@@ -64,8 +64,8 @@ enum { MOE_BF16 = 0, MOE_MXFP8 = 1 };
 /* The layer's shape, following the quantities the pages tune the layer by:
  * hidden size, top-k and expert count [KC §03], expert intermediate size
  * [KC §02], plus the token count and the datatype.
- * Limits: 1 <= T; 1 <= k; 1 <= E <= 1024; H and I multiples of 64 (and of
- * 32 for MXFP8, implied); R = T*k < 2^31; shared_inter 0 or a multiple of 64. */
+ * Limits: 1 <= T; 1 <= k <= 16; 1 <= E <= 1024; H, I and shared_inter
+ * multiples of 64 (of 128 for MXFP8); R = T*k < 2^31; H*E < 2^31. */
 typedef struct moe_shape {
   int32_t tokens;       /* T */
   int32_t hidden;       /* H */
@@ -170,7 +170,9 @@ int moe_dispatch(const moe_shape *shape, const uint16_t *x,
  * a = silu(X w_gate[e]) * (X w_up[e]) (SwiGLU fused in the GEMM epilogue),
  * y = a w_down[e].  x_perm/x_scale as written by moe_dispatch, offsets
  * [E+1], packed from moe_prepare_weights, y [R][H] bf16 (device).  The
- * intermediate activations live in the workspace. */
+ * intermediate activations live in the workspace.  MXFP8: the gate/up GEMM
+ * reads E4M3 codes with their E8M0 scales, the SwiGLU epilogue quantises a
+ * along I (32-wide blocks) and the down GEMM reads those codes [KC §02]. */
 int moe_expert_ffn(const moe_shape *shape, const void *x_perm,
                    const uint8_t *x_scale, const int32_t *offsets,
                    const void *packed, uint16_t *y, void *ws, size_t ws_bytes,
@@ -207,7 +209,11 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched,
  * routing, else NULL); dws [H*Is | H*Is | Is*H] fp32 = shared expert's
  * d(gate), d(up), d(down) (NULL without a shared expert); dtopk_w [T][k]
  * fp32 = gradient of the routing weights (may be NULL).  Every output is
- * fully written (experts that received no rows get zero gradients). */
+ * fully written (experts that received no rows get zero gradients).
+ * MXFP8: the two data-gradient GEMMs read MX copies of dY (along H) and of
+ * dg|du (along I) against weights quantised along the same axes; the weight
+ * gradients are bf16 products of the forward's MX round trips and the bf16
+ * gradients. */
 int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched,
                   const uint16_t *dout, const uint16_t *x,
                   const uint16_t *w_router, const void *saved,
@@ -226,10 +232,13 @@ typedef struct moe_saved_view {
   int32_t *offsets;   /* [E+1] */
   int32_t *perm;      /* [R] */
   int32_t *inv_perm;  /* [R] */
-  void *x_perm;       /* bf16 [R][H], or E4M3 [R][H] */
+  void *x_perm;       /* bf16 [R][H] (bf16), or E4M3 codes [R][H] (MXFP8) */
   uint8_t *x_scale;   /* E8M0 [R][H/32] (MXFP8) */
+  uint16_t *x_hat;    /* bf16 [R][H]: MX round trip of the dispatched rows (MXFP8) */
   uint16_t *gu;       /* bf16 [R][2I]: g and u, interleaved in 32-column blocks */
   uint16_t *act;      /* bf16 [R][I]: a (bf16) or its MX round trip (MXFP8) */
+  uint8_t *act_q;     /* E4M3 [R][I] (MXFP8) */
+  uint8_t *act_scale; /* E8M0 [R][I/32] (MXFP8) */
   uint16_t *y;        /* bf16 [R][H] */
   uint16_t *y_shared; /* bf16 [T][H] (shared expert) */
 } moe_saved_view;

@@ -44,7 +44,7 @@ class MoeSched(ctypes.Structure):
 class MoeSavedView(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in (
         "topk_idx", "topk_w", "logits", "counts", "offsets", "perm", "inv_perm",
-        "x_perm", "x_scale", "gu", "act", "y", "y_shared")]
+        "x_perm", "x_scale", "x_hat", "gu", "act", "act_q", "act_scale", "y", "y_shared")]
 
 
 # name -> (restype, argtypes); keep in the order of include/moe.h

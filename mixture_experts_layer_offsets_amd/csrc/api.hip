@@ -6,6 +6,10 @@
 // Expert FFN, Combine e a fusão ponderada final" (kucoin.com news flash "O MoK
 // do Cursor alcança aumento de desempenho de 2,37x no NVIDIA GB300 NVL72",
 // §03) -- and its backward mirrors the forward's data movement (§01, §02).
+// With MXFP8 the activations entering each GEMM are E4M3 codes with E8M0
+// scales (quantised in dispatch and in the SwiGLU epilogue, §02), the weights
+// are pre-quantised along each GEMM's contraction axis, and the weight
+// gradients run in bf16 on the MX round trips.
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -47,22 +51,38 @@ int check_shape(const moe_shape *s, Dims *d) {
   if (s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
   const long R = (long)s->tokens * s->top_k;
   if (R >= (1L << 31)) return MOE_ERR_INVALID_ARG;
-  if (s->hidden % 64 || s->inter % 64 || s->shared_inter % 64) return MOE_ERR_UNSUPPORTED;
+  const int mult = s->dtype == MOE_MXFP8 ? 128 : 64;
+  if (s->hidden % mult || s->inter % mult || s->shared_inter % mult) return MOE_ERR_UNSUPPORTED;
   if (s->experts > 1024 || s->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)s->hidden * s->experts >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
-  if (s->dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;  // MX path: see moe_prepare_weights
   d->T = s->tokens; d->H = s->hidden; d->E = s->experts; d->k = s->top_k; d->I = s->inter;
-  d->Is = s->shared_inter; d->R = R; d->mx = s->dtype == MOE_MXFP8; d->shared = s->shared_inter > 0;
+  d->Is = s->shared_inter; d->R = R; d->mx = s->dtype == MOE_MXFP8;
+  d->shared = s->shared_inter > 0;
   return MOE_OK;
+}
+
+// An MX tensor: E4M3 codes and one E8M0 scale per 32 values of each row.
+struct MxT {
+  uint8_t *q = nullptr, *s = nullptr;
+};
+
+MxT take_mx(Carver &c, long rows, long cols) {
+  MxT t;
+  t.q = c.take<uint8_t>(rows * cols);
+  t.s = c.take<uint8_t>(rows * (cols / 32));
+  return t;
 }
 
 // ---- forward->backward context
 struct Saved {
   int32_t *idx; float *w; float *logits;
   int32_t *counts, *offsets, *tile_start, *order, *perm, *inv;
-  uint16_t *x_perm;   // bf16 rows (or the MX round trip of the rows)
-  uint16_t *gu, *act, *y;
+  uint16_t *x_perm;   // bf16 rows; with MXFP8 their MX round trip
+  uint16_t *gu, *act, *y;  // act: with MXFP8 the round trip of a
   uint16_t *gu_s, *act_s, *y_s;
+  MxT xq, aq;         // MXFP8: dispatched rows, activations
+  uint16_t *xhat_s;   // MXFP8 shared expert: round trip of x
+  MxT xq_s, aq_s;
 };
 
 size_t carve_saved(const Dims &d, void *base, Saved *s) {
@@ -81,10 +101,19 @@ size_t carve_saved(const Dims &d, void *base, Saved *s) {
   t.gu = c.take<uint16_t>(d.R * 2 * d.I);
   t.act = c.take<uint16_t>(d.R * d.I);
   t.y = c.take<uint16_t>(d.R * d.H);
+  if (d.mx) {
+    t.xq = take_mx(c, d.R, d.H);
+    t.aq = take_mx(c, d.R, d.I);
+  }
   if (d.shared) {
     t.gu_s = c.take<uint16_t>(d.T * 2 * d.Is);
     t.act_s = c.take<uint16_t>(d.T * d.Is);
     t.y_s = c.take<uint16_t>(d.T * d.H);
+    if (d.mx) {
+      t.xhat_s = c.take<uint16_t>(d.T * d.H);
+      t.xq_s = take_mx(c, d.T, d.H);
+      t.aq_s = take_mx(c, d.T, d.Is);
+    }
   }
   if (s) *s = t;
   return c.off;
@@ -98,9 +127,11 @@ struct Work {
   // standalone layout / expert FFN
   int32_t *tile_start, *order;
   uint16_t *act, *gu;
+  MxT aq;
   // backward
   uint16_t *dy, *dh, *dX, *wrT, *dh_s, *dxs;
   float *dw, *dsel;
+  MxT dyq, dhq, doutq, dhq_s;
 };
 
 size_t carve_work(const Dims &d, void *base, Work *w) {
@@ -118,6 +149,7 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   // forward-only pieces (standalone expert FFN)
   t.act = c.take<uint16_t>(d.R * d.I);
   t.gu = c.take<uint16_t>(d.R * 2 * d.I);
+  if (d.mx) t.aq = take_mx(c, d.R, d.I);
   const size_t fwd_end = c.off;
   // backward-only pieces share the same bytes
   c.off = union_start;
@@ -127,34 +159,53 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   t.dw = c.take<float>(d.R);
   t.dsel = c.take<float>(d.R);
   t.wrT = c.take<uint16_t>(d.E * d.H);
+  if (d.mx) {
+    t.dyq = take_mx(c, d.R, d.H);
+    t.dhq = take_mx(c, d.R, 2 * d.I);
+  }
   if (d.shared) {
     t.dh_s = c.take<uint16_t>(d.T * 2 * d.Is);
     t.dxs = c.take<uint16_t>(d.T * d.H);
+    if (d.mx) {
+      t.doutq = take_mx(c, d.T, d.H);
+      t.dhq_s = take_mx(c, d.T, 2 * d.Is);
+    }
   }
   if (c.off < fwd_end) c.off = fwd_end;
   if (w) *w = t;
   return c.off;
 }
 
-// ---- packed weights
+// ---- packed weights: one expert set (routed: G = E; shared: G = 1)
+struct WSet {
+  uint16_t *guT, *dT, *gu, *d;  // bf16: [G][2I][H], [G][H][I], [G][H][2I], [G][I][H]
+  MxT guTq, dTq, guq, dq;       // MXFP8 copies, each quantised along its contraction axis
+};
+
+WSet take_wset(Carver &c, long G, long H, long I, bool mx) {
+  WSet t{};
+  t.guT = c.take<uint16_t>(G * 2 * I * H);
+  t.dT = c.take<uint16_t>(G * H * I);
+  t.gu = c.take<uint16_t>(G * H * 2 * I);
+  t.d = c.take<uint16_t>(G * I * H);
+  if (mx) {
+    t.guTq = take_mx(c, G * 2 * I, H);
+    t.dTq = take_mx(c, G * H, I);
+    t.guq = take_mx(c, G * H, 2 * I);
+    t.dq = take_mx(c, G * I, H);
+  }
+  return t;
+}
+
 struct Packed {
-  uint16_t *guT, *dT, *gu, *d;      // routed experts
-  uint16_t *sguT, *sdT, *sgu, *sd;  // shared expert
+  WSet r, s;  // routed experts, shared expert
 };
 
 size_t carve_packed(const Dims &d, const void *base, Packed *p) {
   Carver c((void *)base);
   Packed t{};
-  t.guT = c.take<uint16_t>(d.E * 2 * d.I * d.H);  // [E][2I][H]
-  t.dT = c.take<uint16_t>(d.E * d.H * d.I);       // [E][H][I]
-  t.gu = c.take<uint16_t>(d.E * d.H * 2 * d.I);   // [E][H][2I]
-  t.d = c.take<uint16_t>(d.E * d.I * d.H);        // [E][I][H]
-  if (d.shared) {
-    t.sguT = c.take<uint16_t>(2 * d.Is * d.H);
-    t.sdT = c.take<uint16_t>(d.H * d.Is);
-    t.sgu = c.take<uint16_t>(d.H * 2 * d.Is);
-    t.sd = c.take<uint16_t>(d.Is * d.H);
-  }
+  t.r = take_wset(c, d.E, d.H, d.I, d.mx);
+  if (d.shared) t.s = take_wset(c, 1, d.H, d.Is, d.mx);
   if (p) *p = t;
   return c.off;
 }
@@ -173,65 +224,117 @@ struct Stages {
   }
 };
 
+// Pack one expert set: gate/up interleaved in 32-wide blocks (g block, then
+// u block, per 64) so one GEMM tile holds matching g and u columns; every
+// GEMM operand contraction-contiguous.  With MXFP8 each packed copy is then
+// quantised along its rows, i.e. along its GEMM's contraction axis (the
+// interleave moves whole 32-blocks, so blocks never mix g and u).
+void pack_wset(const WSet &w, int G, int H, int I, const uint16_t *wg, const uint16_t *wu,
+               const uint16_t *wd, bool mx, hipStream_t s) {
+  launch_transpose_pack(wg, w.guT, G, H, I, 2 * I, 64, 0, s);
+  launch_transpose_pack(wu, w.guT, G, H, I, 2 * I, 64, 32, s);
+  launch_transpose_pack(wd, w.dT, G, I, H, H, 32, 0, s);
+  launch_interleave_copy(wg, w.gu, G, H, I, 2 * I, 64, 0, s);
+  launch_interleave_copy(wu, w.gu, G, H, I, 2 * I, 64, 32, s);
+  launch_interleave_copy(wd, w.d, G, I, H, H, 32, 0, s);  // plain copy, [G][I][H]
+  if (mx) {
+    launch_quant_rows_mx(w.guT, G * 2 * I, H, w.guTq.q, w.guTq.s, s);  // along H
+    launch_quant_rows_mx(w.dT, G * H, I, w.dTq.q, w.dTq.s, s);         // along I
+    launch_quant_rows_mx(w.gu, G * H, 2 * I, w.guq.q, w.guq.s, s);     // along I
+    launch_quant_rows_mx(w.d, G * I, H, w.dq.q, w.dq.s, s);            // along H
+  }
+}
+
 // Expert FFN over row-ragged groups: a = silu(X Wg) * (X Wu); y = a Wd.
-void ffn_forward(const uint16_t *X, long ldx, const int32_t *offsets, const int32_t *tiles,
-                 int G, long max_rows, long H, long I, const uint16_t *guT, const uint16_t *dT,
-                 uint16_t *act, uint16_t *gu, uint16_t *y, hipStream_t s,
-                 const Stages *st = nullptr, int mark = 0) {
+// bf16: rows x.  MXFP8: rows xq (codes + scales); a is quantised in the
+// gate/up epilogue (codes and scales into aq, round trip into act) and the
+// down GEMM consumes the codes.
+void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_t *tiles, int G,
+                 long max_rows, long H, long I, const WSet &W, bool mx, uint16_t *act,
+                 uint16_t *gu, MxT aq, uint16_t *y, hipStream_t s, const Stages *st = nullptr,
+                 int mark = 0) {
   GemmArgs p{};
-  p.A = X; p.lda = ldx;
-  p.B = guT; p.ldb = H; p.sB = 2 * I * H;
   p.C = act; p.ldc = I;
   p.C2 = gu; p.ldc2 = 2 * I;
   p.offsets = offsets; p.tile_start = tiles;
   p.G = G; p.N = (int)(2 * I); p.K = (int)H;
-  launch_gemm_rows(p, EPI_SWIGLU, true, (int)max_rows, s);
+  p.lda = H; p.ldb = H; p.sB = 2 * I * H;
+  if (!mx) {
+    p.A = x; p.B = W.guT;
+    launch_gemm_rows(p, EPI_SWIGLU, true, (int)max_rows, s);
+  } else {
+    p.A = (const uint16_t *)xq.q; p.B = (const uint16_t *)W.guTq.q;
+    const MxOperands m{xq.s, W.guTq.s, 2 * I * (H / 32), aq.q, aq.s};
+    launch_gemm_rows_mx(p, m, EPI_SWIGLU, (int)max_rows, s);
+  }
   if (st) st->mark(mark);
   GemmArgs q{};
-  q.A = act; q.lda = I;
-  q.B = dT; q.ldb = I; q.sB = H * I;
   q.C = y; q.ldc = H;
   q.offsets = offsets; q.tile_start = tiles;
   q.G = G; q.N = (int)H; q.K = (int)I;
-  launch_gemm_rows(q, EPI_BF16, true, (int)max_rows, s);
+  q.lda = I; q.ldb = I; q.sB = H * I;
+  if (!mx) {
+    q.A = act; q.B = W.dT;
+    launch_gemm_rows(q, EPI_BF16, true, (int)max_rows, s);
+  } else {
+    q.A = (const uint16_t *)aq.q; q.B = (const uint16_t *)W.dTq.q;
+    const MxOperands m{aq.s, W.dTq.s, H * (I / 32), nullptr, nullptr};
+    launch_gemm_rows_mx(q, m, EPI_BF16, (int)max_rows, s);
+  }
   if (st) st->mark(mark + 1);
 }
 
 // Backward of the expert FFN for row-ragged groups given dY (rows' output
-// gradient).  Writes dh (packed dg|du), dX, and the weight gradients.
-void ffn_backward(const uint16_t *X, long ldx, const uint16_t *dY, long lddy,
-                  const int32_t *offsets, const int32_t *tiles, const int32_t *order, int G,
-                  long max_rows, long H, long I, const uint16_t *gu_w, const uint16_t *d_w,
-                  const uint16_t *gu_saved, const uint16_t *act, uint16_t *dh, uint16_t *dX,
-                  float *dWg, float *dWu, float *dWd, hipStream_t s,
-                  const Stages *st = nullptr, int mark = 0) {
+// gradient, bf16, [rows][H]).  Writes dh (packed dg|du), dX and the weight
+// gradients.  With MXFP8 the two data-gradient GEMMs consume MX copies of dY
+// and dh (quantised here into dyq, dhq); the weight gradients use the bf16
+// tensors (X and act then hold the forward's MX round trips).
+void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
+                  const int32_t *tiles, const int32_t *order, int G, long max_rows, long H,
+                  long I, const WSet &W, bool mx, MxT dyq, MxT dhq, const uint16_t *gu_saved,
+                  const uint16_t *act, uint16_t *dh, uint16_t *dX, float *dWg, float *dWu,
+                  float *dWd, hipStream_t s, const Stages *st = nullptr, int mark = 0) {
   GemmArgs a{};  // dA = dY Wd^T, SwiGLU backward in the epilogue -> dh
-  a.A = dY; a.lda = lddy;
-  a.B = d_w; a.ldb = H; a.sB = I * H;
   a.C = dh; a.ldc = 2 * I;
   a.aux = gu_saved; a.ldaux = 2 * I;
   a.offsets = offsets; a.tile_start = tiles;
   a.G = G; a.N = (int)I; a.K = (int)H;
-  launch_gemm_rows(a, EPI_SWIGLU_BWD, true, (int)max_rows, s);
+  a.lda = H; a.ldb = H; a.sB = I * H;
+  if (!mx) {
+    a.A = dY; a.B = W.d;
+    launch_gemm_rows(a, EPI_SWIGLU_BWD, true, (int)max_rows, s);
+  } else {
+    launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
+    a.A = (const uint16_t *)dyq.q; a.B = (const uint16_t *)W.dq.q;
+    const MxOperands m{dyq.s, W.dq.s, I * (H / 32), nullptr, nullptr};
+    launch_gemm_rows_mx(a, m, EPI_SWIGLU_BWD, (int)max_rows, s);
+  }
   if (st) st->mark(mark);
   GemmArgs b{};  // dWd = act^T dY
   b.A = act; b.lda = I;
-  b.B = dY; b.ldb = lddy;
+  b.B = dY; b.ldb = H;
   b.C = dWd; b.ldc = H; b.sC = I * H;
   b.offsets = offsets; b.order = order;
   b.G = G; b.M = (int)I; b.N = (int)H;
   launch_gemm_wgrad(b, EPI_F32, s);
   if (st) st->mark(mark + 1);
   GemmArgs c{};  // dX = dh Wgu^T
-  c.A = dh; c.lda = 2 * I;
-  c.B = gu_w; c.ldb = 2 * I; c.sB = H * 2 * I;
   c.C = dX; c.ldc = H;
   c.offsets = offsets; c.tile_start = tiles;
   c.G = G; c.N = (int)H; c.K = (int)(2 * I);
-  launch_gemm_rows(c, EPI_BF16, true, (int)max_rows, s);
+  c.lda = 2 * I; c.ldb = 2 * I; c.sB = H * 2 * I;
+  if (!mx) {
+    c.A = dh; c.B = W.gu;
+    launch_gemm_rows(c, EPI_BF16, true, (int)max_rows, s);
+  } else {
+    launch_quant_rows_mx(dh, (int)max_rows, (int)(2 * I), dhq.q, dhq.s, s);
+    c.A = (const uint16_t *)dhq.q; c.B = (const uint16_t *)W.guq.q;
+    const MxOperands m{dhq.s, W.guq.s, H * (2 * I / 32), nullptr, nullptr};
+    launch_gemm_rows_mx(c, m, EPI_BF16, (int)max_rows, s);
+  }
   if (st) st->mark(mark + 2);
   GemmArgs e{};  // dWg | dWu = X^T dh
-  e.A = X; e.lda = ldx;
+  e.A = X; e.lda = H;
   e.B = dh; e.ldb = 2 * I;
   e.C = dWg; e.C2 = dWu; e.ldc = I; e.sC = H * I;
   e.offsets = offsets; e.order = order;
@@ -285,27 +388,8 @@ int moe_prepare_weights(const moe_shape *shape, const uint16_t *w_gate, const ui
   Packed p;
   carve_packed(d, packed, &p);
   hipStream_t s = S(stream);
-  const int E = (int)d.E, H = (int)d.H, I = (int)d.I;
-  // forward gate/up: [E][2I][H], gate rows at 64-blocks' first half, up second
-  launch_transpose_pack(w_gate, p.guT, E, H, I, 2 * I, 64, 0, s);
-  launch_transpose_pack(w_up, p.guT, E, H, I, 2 * I, 64, 32, s);
-  launch_transpose_pack(w_down, p.dT, E, I, H, H, 32, 0, s);  // [E][H][I]
-  launch_interleave_copy(w_gate, p.gu, E, H, I, 2 * I, 64, 0, s);
-  launch_interleave_copy(w_up, p.gu, E, H, I, 2 * I, 64, 32, s);
-  if (hipMemcpyAsync(p.d, w_down, (size_t)d.E * d.I * d.H * 2, hipMemcpyDeviceToDevice, s) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
-  if (d.shared) {
-    const int Is = (int)d.Is;
-    launch_transpose_pack(ws_gate, p.sguT, 1, H, Is, 2 * Is, 64, 0, s);
-    launch_transpose_pack(ws_up, p.sguT, 1, H, Is, 2 * Is, 64, 32, s);
-    launch_transpose_pack(ws_down, p.sdT, 1, Is, H, H, 32, 0, s);
-    launch_interleave_copy(ws_gate, p.sgu, 1, H, Is, 2 * Is, 64, 0, s);
-    launch_interleave_copy(ws_up, p.sgu, 1, H, Is, 2 * Is, 64, 32, s);
-    if (hipMemcpyAsync(p.sd, ws_down, (size_t)d.Is * d.H * 2, hipMemcpyDeviceToDevice, s) !=
-        hipSuccess)
-      return MOE_ERR_HIP;
-  }
+  pack_wset(p.r, (int)d.E, (int)d.H, (int)d.I, w_gate, w_up, w_down, d.mx, s);
+  if (d.shared) pack_wset(p.s, 1, (int)d.H, (int)d.Is, ws_gate, ws_up, ws_down, d.mx, s);
   return hip_status();
 }
 
@@ -378,8 +462,8 @@ int moe_expert_ffn(const moe_shape *shape, const void *x_perm, const uint8_t *x_
   Dims d;
   int rc = check_shape(shape, &d);
   if (rc) return rc;
-  (void)x_scale;
   if (!x_perm || !offsets || !packed || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.mx && !x_scale) return MOE_ERR_INVALID_ARG;
   Work w;
   if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
   Packed p;
@@ -387,8 +471,11 @@ int moe_expert_ffn(const moe_shape *shape, const void *x_perm, const uint8_t *x_
   hipStream_t s = S(stream);
   // the GEMM's tile prefix, derived on the device from the offsets
   launch_tile_starts(offsets, (int)d.E, kTileM, w.tile_start, s);
-  ffn_forward((const uint16_t *)x_perm, d.H, offsets, w.tile_start, (int)d.E, d.R, d.H, d.I,
-              p.guT, p.dT, w.act, w.gu, y, s);
+  MxT xq;
+  xq.q = (uint8_t *)x_perm;
+  xq.s = (uint8_t *)x_scale;
+  ffn_forward((const uint16_t *)x_perm, xq, offsets, w.tile_start, (int)d.E, d.R, d.H, d.I, p.r,
+              d.mx, w.act, w.gu, w.aq, y, s);
   return hip_status();
 }
 
@@ -412,7 +499,13 @@ int moe_saved_pointers(const moe_shape *shape, void *saved, moe_saved_view *view
   memset(view, 0, sizeof(*view));
   view->topk_idx = s.idx; view->topk_w = s.w; view->logits = s.logits;
   view->counts = s.counts; view->offsets = s.offsets; view->perm = s.perm;
-  view->inv_perm = s.inv; view->x_perm = s.x_perm; view->x_scale = nullptr;
+  view->inv_perm = s.inv;
+  if (d.mx) {
+    view->x_perm = s.xq.q; view->x_scale = s.xq.s; view->x_hat = s.x_perm;
+    view->act_q = s.aq.q; view->act_scale = s.aq.s;
+  } else {
+    view->x_perm = s.x_perm;
+  }
   view->gu = s.gu; view->act = s.act; view->y = s.y; view->y_shared = s.y_s;
   return MOE_OK;
 }
@@ -424,7 +517,6 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   Dims d;
   int rc = check_shape(shape, &d);
   if (rc) return rc;
-  (void)sched;
   if (!x || !packed || !out || !saved || !ws) return MOE_ERR_INVALID_ARG;
   const bool router = w_router != nullptr;
   if (router == (topk_idx_in != nullptr) || (topk_idx_in != nullptr) != (topk_w_in != nullptr))
@@ -465,16 +557,21 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   launch_layout(sv.idx, (int)d.R, E, w.chunk_counts, sv.counts, sv.offsets, sv.perm, sv.inv,
                 sv.tile_start, kTileM, sv.order, s);
   st.mark(1);
-  // Dispatch
-  launch_dispatch_bf16(x, sv.perm, sv.x_perm, (int)d.R, k, H, s);
+  // Dispatch (MXFP8: quantised while gathered; the round trip is kept for the
+  // weight gradients)
+  if (d.mx)
+    launch_dispatch_mx(x, sv.perm, sv.xq.q, sv.xq.s, sv.x_perm, (int)d.R, k, H, s);
+  else
+    launch_dispatch_bf16(x, sv.perm, sv.x_perm, (int)d.R, k, H, s);
   st.mark(2);
   // Expert FFN
-  ffn_forward(sv.x_perm, H, sv.offsets, sv.tile_start, E, d.R, d.H, d.I, p.guT, p.dT, sv.act,
-              sv.gu, sv.y, s, &st, 3);
+  ffn_forward(sv.x_perm, sv.xq, sv.offsets, sv.tile_start, E, d.R, d.H, d.I, p.r, d.mx, sv.act,
+              sv.gu, sv.aq, sv.y, s, &st, 3);
   if (d.shared) {
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
-    ffn_forward(x, H, w.dense_offsets, w.dense_tiles, 1, d.T, d.H, d.Is, p.sguT, p.sdT,
-                sv.act_s, sv.gu_s, sv.y_s, s);
+    if (d.mx) launch_dispatch_mx(x, nullptr, sv.xq_s.q, sv.xq_s.s, sv.xhat_s, T, 1, H, s);
+    ffn_forward(x, sv.xq_s, w.dense_offsets, w.dense_tiles, 1, d.T, d.H, d.Is, p.s, d.mx,
+                sv.act_s, sv.gu_s, sv.aq_s, sv.y_s, s);
   }
   st.mark(5);
   // Combine + final weighted fusion
@@ -491,7 +588,6 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   Dims d;
   int rc = check_shape(shape, &d);
   if (rc) return rc;
-  (void)sched;
   if (!dout || !x || !saved || !packed || !dx || !dw_gate || !dw_up || !dw_down || !ws)
     return MOE_ERR_INVALID_ARG;
   const bool router = w_router != nullptr;
@@ -515,13 +611,15 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
                          s);
   st.mark(1);
   // Expert FFN backward
-  ffn_backward(sv.x_perm, H, w.dy, H, sv.offsets, sv.tile_start, sv.order, E, d.R, d.H, d.I,
-               p.gu, p.d, sv.gu, sv.act, w.dh, w.dX, dw_gate, dw_up, dw_down, s, &st, 2);
+  ffn_backward(sv.x_perm, w.dy, sv.offsets, sv.tile_start, sv.order, E, d.R, d.H, d.I, p.r,
+               d.mx, w.dyq, w.dhq, sv.gu, sv.act, w.dh, w.dX, dw_gate, dw_up, dw_down, s, &st,
+               2);
   if (d.shared) {
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
     float *dWsg = dws, *dWsu = dws + d.H * d.Is, *dWsd = dws + 2 * d.H * d.Is;
-    ffn_backward(x, H, dout, H, w.dense_offsets, w.dense_tiles, w.dense_order, 1, d.T, d.H,
-                 d.Is, p.sgu, p.sd, sv.gu_s, sv.act_s, w.dh_s, w.dxs, dWsg, dWsu, dWsd, s);
+    ffn_backward(d.mx ? sv.xhat_s : x, dout, w.dense_offsets, w.dense_tiles, w.dense_order, 1,
+                 d.T, d.H, d.Is, p.s, d.mx, w.doutq, w.dhq_s, sv.gu_s, sv.act_s, w.dh_s, w.dxs,
+                 dWsg, dWsu, dWsd, s);
   }
   st.mark(6);
   // Router backward and reverse-dispatch

@@ -76,6 +76,21 @@ struct GemmArgs {
 // number of rows (sizes the grid).
 void launch_gemm_rows(const GemmArgs &p, int epi, bool b_kcontig, int max_rows, hipStream_t s);
 
+// Row-ragged grouped GEMM on MXFP8 operands (E4M3 codes + E8M0 scales per 32
+// along K): A codes [rows][K] with scales [rows][K/32]; B codes [G][N][K]
+// with scales [G][N][K/32].  Epilogues: EPI_BF16, EPI_SWIGLU (with
+// p.mx_out: a quantised along I into codes/scales, and its bf16 round trip
+// into p.C), EPI_SWIGLU_BWD.
+struct MxOperands {
+  const uint8_t *a_scale;   // [rows][K/32]
+  const uint8_t *b_scale;   // [G][N][K/32]
+  long sBs;                 // per-group stride of b_scale (bytes)
+  uint8_t *q_out;           // SwiGLU MX epilogue: a codes [rows][I]
+  uint8_t *s_out;           // SwiGLU MX epilogue: a scales [rows][I/32]
+};
+void launch_gemm_rows_mx(const GemmArgs &p, const MxOperands &mx, int epi, int max_rows,
+                         hipStream_t s);
+
 // Weight-gradient grouped GEMM: for group g, C_g[M][N] = sum over rows
 // [offsets[g], offsets[g+1]) of A[row][M]^T B[row][N] (both row-major with the
 // summed rows outermost).

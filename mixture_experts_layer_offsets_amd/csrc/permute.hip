@@ -17,6 +17,7 @@
 // and reduces in a fixed order.
 #include "common.h"
 #include "kernels.h"
+#include "mx_device.h"
 
 namespace moe {
 
@@ -25,29 +26,6 @@ namespace moe {
 //   s = clamp(floor(log2 amax) - 8, -127, 127), scale code s + 127
 //   code_i = E4M3(clamp(v_i * 2^-s, -448, 448)), nearest-even;
 //   an all-zero block gets scale code 0.
-
-__device__ __forceinline__ uint32_t e4m3_encode(float v, bool neg) {
-  const float a = fabsf(v);
-  const uint32_t sign = neg ? 0x80u : 0u;
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // spacing 2^-9
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // round to 3 mantissa bits
-  const int e = (int)(r >> 23) - 127;
-  return sign | ((uint32_t)(e + 7) << 3) | ((r >> 20) & 7u);
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t ex = (c >> 3) & 15u, m = c & 7u;
-  const float mag = ex ? ldexpf((float)(8u + m), (int)ex - 10) : ldexpf((float)m, -9);
-  return (c & 0x80u) ? -mag : mag;
-}
-
-__device__ __forceinline__ int floor_log2(float a) {  // a > 0
-  const uint32_t u = __float_as_uint(a);
-  const int ex = (int)(u >> 23);
-  if (ex) return ex - 127;
-  return -149 + (31 - __clz(u & 0x7FFFFFu));
-}
 
 // Quantise 32 values; writes 32 codes (two uint4) and returns the scale code.
 // `deq` receives the dequantised values (may be null).

@@ -147,13 +147,15 @@ def _swiglu_rows(Xhat, Wg, Wu, Wd, mx, R):
 
     SwiGLU is named as the expert activation [KC §02]; reading: the gate
     projection goes through silu, multiplies the up projection, and the down
-    projection follows, with no biases.  g and u are held in fp32; a is
+    projection follows, with no biases.  g and u are held in fp32 and a is
+    formed in fp32 (the GEMM accumulator's precision), so the bf16 rounding or
+    MX quantisation of a decides from an fp32 value as the kernel does; a is
     stored as bf16, or with MXFP8 quantised along the intermediate axis (the
     SwiGLU epilogue quantises [KC §02]); Y is stored as bf16.
     """
     g = R.f32(Xhat @ Wg)
     u = R.f32(Xhat @ Wu)
-    a = silu(g) * u
+    a = R.f32(silu(g) * u)
     ahat = mx_roundtrip(a, axis=1) if mx else R.bf16(a)
     Y = R.bf16(ahat @ Wd)
     return g, u, ahat, Y
@@ -373,6 +375,20 @@ class _LazyWeights:
         self.keep = keep
         self.cache = {}
 
+    def prefetch(self, experts, threads=8):
+        """Decode several experts at once (numpy releases the GIL in the
+        elementwise work, so threads overlap); the cache grows to hold them."""
+        from concurrent.futures import ThreadPoolExecutor
+        todo = [int(e) for e in dict.fromkeys(experts) if int(e) not in self.cache]
+        self.keep = max(self.keep, len(self.cache) + len(todo))
+
+        def one(e):
+            return _weights(dict(w_gate=self.src[0][e], w_up=self.src[1][e],
+                                 w_down=self.src[2][e]), self.mx)
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            for e, We in zip(todo, ex.map(one, todo)):
+                self.cache[e] = We
+
     def __getitem__(self, e):
         if e in self.cache:
             self.cache[e] = self.cache.pop(e)          # most recently used last
@@ -460,7 +476,7 @@ class TokenEvaluator:
         return dict(dw=dw, dx=self.R.bf16(acc))
 
 
-def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False):
+def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, weights=None):
     """dW_down[e, i, :], dW_gate[e, :, i], dW_up[e, :, i] for chosen columns i.
 
     Sums over the rows routed to expert e (found from the routing by
@@ -468,16 +484,18 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False):
     that the chosen columns fall in.  For sampled checks at full size.
     Router routing is evaluated in full (it is cheap); the FFN is not.
     With ``shared`` the expert is the shared one: every token, weight one.
+    ``weights`` may pass the decoded weights of the expert (as a
+    TokenEvaluator holds them) to skip decoding them again.
     """
     R = _Round(False)
     x = _val(inp["x"])
     dout = _val(inp["dout"] if dout is None else dout)
     if shared:
-        We = _LazyWeights(inp, mx, shared=True)[0]
+        We = weights if weights is not None else _LazyWeights(inp, mx, shared=True)[0]
         t = np.arange(x.shape[0])
         wrow = np.ones(x.shape[0])
     else:
-        We = _LazyWeights(inp, mx)[e]
+        We = weights if weights is not None else _LazyWeights(inp, mx)[e]
         if inp.get("topk_idx") is None:
             L = router_logits(x, inp["w_router"], inp.get("bias"))
             idx, w = topk_softmax(L, k)
@@ -495,7 +513,7 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False):
     bc = np.concatenate([np.arange(b * 32, b * 32 + 32) for b in blocks])
     g = R.f32(xh @ We["g"][:, bc])
     u = R.f32(xh @ We["u"][:, bc])
-    a = silu(g) * u
+    a = R.f32(silu(g) * u)
     ah = mx_roundtrip(a, axis=1) if mx else R.bf16(a)
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
     dA = R.f32(dYq @ We["d_b"][bc, :].T)

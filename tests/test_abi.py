@@ -123,3 +123,22 @@ def test_strerror(lib):
     assert m.moe_strerror(0) == "ok"
     assert "workspace" in m.moe_strerror(_lib.MOE_ERR_WORKSPACE)
     assert m.moe_strerror(12345) == "unknown error"
+
+
+def test_mx_sizes_and_shape_rules(lib):
+    """MXFP8 needs H, I and the shared I in multiples of 128; its buffers add
+    the E4M3 codes and E8M0 scales to the bf16 ones."""
+    bf = m.Shape(2048, 7168, 6, 8, 2048)
+    mx = m.Shape(2048, 7168, 6, 8, 2048, 0, m.MOE_MXFP8)
+    R, H, I, E = 2048 * 8, 7168, 2048, 6
+    assert m.moe_saved_bytes(mx) >= m.moe_saved_bytes(bf) + R * (H + I) * 33 // 32
+    assert m.moe_workspace_bytes(mx) >= m.moe_workspace_bytes(bf) + R * (H + 2 * I) * 33 // 32
+    assert m.moe_packed_weight_bytes(mx) >= \
+        m.moe_packed_weight_bytes(bf) + 2 * 3 * E * H * I * 33 // 32
+    assert m.moe_workspace_bytes(m.Shape(64, 256, 8, 2, 128, 0, m.MOE_MXFP8)) > 0
+    for bad in (m.Shape(64, 192, 8, 2, 128, 0, m.MOE_MXFP8),
+                m.Shape(64, 256, 8, 2, 192, 0, m.MOE_MXFP8),
+                m.Shape(64, 256, 8, 2, 128, 64, m.MOE_MXFP8)):
+        assert m.moe_workspace_bytes(bad) == 0
+        assert lib.moe_route(ctypes.byref(bad.c()), 1 << 40, 1 << 40, 1 << 40, None) == \
+            _lib.MOE_ERR_UNSUPPORTED
