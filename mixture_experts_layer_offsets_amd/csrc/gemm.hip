@@ -27,6 +27,7 @@
 // about what a 256 x 256 bf16 tile consumes at full MFMA rate -- so the
 // kernels are co-limited by operand feed and matrix issue.
 #include "gemm_common.h"
+#include "tile_epilogue.h"
 
 namespace moe {
 
@@ -316,7 +317,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
     __syncthreads();
   }
   if (kt < nk) compute(L0);
-  epilogue<false, EPI>(p, acc, g, m0, n0, rowbase, Mg, wm0, wn0, lane);
+  const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
+  if constexpr (EPI == EPI_BF16)
+    tile_epi_bf16(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+  else if constexpr (EPI == EPI_SWIGLU)
+    tile_epi_swiglu<false>(p, nullptr, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+  else
+    tile_epi_swiglu_bwd(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
 }
 
 template <bool WGRAD, bool B_KC>

@@ -19,58 +19,13 @@
 // maximum is a five-step xor-shuffle reduction.
 #include "gemm_common.h"
 #include "mx_device.h"
+#include "tile_epilogue.h"
 
 namespace moe {
 
 constexpr int MXK = 128;  // K bytes (= fp8 values) per stage
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// SwiGLU epilogue with MX output for the 32-row block IB of a wave's tile:
-// a = silu(g) u, quantised along I in 32-wide blocks (one block = the 32
-// lanes of a half-wave, so the block maximum is a xor-shuffle reduction);
-// codes and scales go to mx.q_out / mx.s_out, the round trip as bf16 to p.C,
-// and g, u (bf16) to p.C2 when given.
-template <int IB>
-__device__ __forceinline__ void swiglu_mx_rows(const GemmArgs &p, const MxOperands &mx,
-                                               f32x16 (&acc)[4], int m0, int n0, int rowbase,
-                                               int Mg, int wm0, int wn0, int lane) {
-  const int I = p.N / 2;
-  const int ncol = lane & 31;
-#pragma unroll
-  for (int jj = 0; jj < 2; jj++) {
-    const int n = n0 + wn0 + jj * 64 + ncol;  // gate column
-    const bool ncols_ok = n0 + wn0 + jj * 64 < p.N;
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int m = m0 + wm0 + IB * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const float gv = acc[2 * jj][v], uv = acc[2 * jj + 1][v];
-      const float av = silu_f(gv) * uv;
-      float amax = fabsf(av);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-      if (m < Mg && ncols_ok) {
-        int s = -127;
-        if (amax > 0.0f) {
-          s = floor_log2(amax) - 8;
-          s = s < -127 ? -127 : (s > 127 ? 127 : s);
-        }
-        const float sc = fminf(fmaxf(ldexpf(av, -s), -448.0f), 448.0f);
-        const uint32_t code = amax > 0.0f ? e4m3_encode(sc, av < 0.0f) : 0u;
-        const int ai = (n >> 6) * 32 + ncol;
-        const size_t row = (size_t)(rowbase + m);
-        mx.q_out[row * I + ai] = (uint8_t)code;
-        if (ncol == 0) mx.s_out[row * (I / 32) + (n >> 6)] = (uint8_t)(s + 127);
-        ((uint16_t *)p.C)[row * p.ldc + ai] = (uint16_t)f32_to_bf16(ldexpf(e4m3_value(code), s));
-        if (p.C2) {
-          uint16_t *GU = (uint16_t *)p.C2 + row * p.ldc2;
-          GU[n] = (uint16_t)f32_to_bf16(gv);
-          GU[n + 32] = (uint16_t)f32_to_bf16(uv);
-        }
-      }
-    }
-  }
-}
 
 template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_mx_kernel(GemmArgs p, MxOperands mx) {
@@ -205,16 +160,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_mx_kernel(GemmArgs p, MxOperands m
   }
   if (kt < nk) compute(L0, sa0, sb0);
 
-  if constexpr (EPI == EPI_SWIGLU) {
-    if (mx.q_out) {
-      swiglu_mx_rows<0>(p, mx, acc[0], m0, n0, rowbase, Mg, wm0, wn0, lane);
-      swiglu_mx_rows<1>(p, mx, acc[1], m0, n0, rowbase, Mg, wm0, wn0, lane);
-      swiglu_mx_rows<2>(p, mx, acc[2], m0, n0, rowbase, Mg, wm0, wn0, lane);
-      swiglu_mx_rows<3>(p, mx, acc[3], m0, n0, rowbase, Mg, wm0, wn0, lane);
-      return;
-    }
+  const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
+  if constexpr (EPI == EPI_BF16) {
+    tile_epi_bf16(p, acc, L0, L1, t);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (mx.q_out)
+      tile_epi_swiglu<true>(p, &mx, acc, L0, L1, t);
+    else
+      tile_epi_swiglu<false>(p, nullptr, acc, L0, L1, t);
+  } else {
+    tile_epi_swiglu_bwd(p, acc, L0, L1, t);
   }
-  epilogue<false, EPI>(p, acc, g, m0, n0, rowbase, Mg, wm0, wn0, lane);
 }
 
 void launch_gemm_rows_mx(const GemmArgs &p0, const MxOperands &mx, int epi, int max_rows,

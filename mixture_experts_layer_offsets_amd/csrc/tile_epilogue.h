@@ -1,0 +1,243 @@
+// Row-GEMM epilogues that stage the 256 x 256 output tile in LDS and write
+// it out as whole rows with 16-byte stores.
+//
+// An MFMA accumulator lane holds one column of 4-row runs, so writing it to
+// global memory directly means one 1- or 2-byte store per value, 64 bytes per
+// half-wave at best; the SwiGLU backward also needs the saved g and u of
+// every value.  Both cost more than the tile's MFMAs at these shapes.  Here
+// the tile goes through LDS instead: the two 64 KB operand buffers, free once
+// the K loop is done, hold rows 0-127 (plane 0) and 128-255 (plane 1), each
+// row a whole number of 16-byte chunks with the chunk index XOR-ed by the row
+// (the accumulator layout's row pairs r, r + 4 then fall in different bank
+// groups).  All 256 threads then copy rows out, 16 bytes per lane, 32 or 64
+// lanes per row: full 128-byte lines.  The SwiGLU backward reads its g, u
+// span the same way, row-coalesced into LDS, and writes dg, du in place.
+#pragma once
+
+#include "gemm_common.h"
+#include "mx_device.h"
+
+namespace moe {
+
+// Byte offset of 16-byte chunk `ch` of row `r` in a plane whose rows hold
+// `nch` chunks (a power of two).
+__device__ __forceinline__ int st_off(int r, int ch, int nch) {
+  return (r * nch + (ch ^ (r & (nch - 1)))) << 4;
+}
+
+// Byte offset of byte `b` of row `r`.
+__device__ __forceinline__ int st_byte(int r, int b, int nch) {
+  return st_off(r, b >> 4, nch) + (b & 15);
+}
+
+// Copy `rows` staged rows (nch chunks each) to dst (row pitch ld bytes):
+// rows < rows_valid, chunks whose first byte is < col_bytes.
+__device__ __forceinline__ void copy_rows_out(const uint8_t *plane, int nch, int rows,
+                                              int rows_valid, int col_bytes, uint8_t *dst,
+                                              long ld, int tid) {
+  const int n = rows * nch;
+  for (int idx = tid; idx < n; idx += NT) {
+    const int r = idx / nch, ch = idx - (idx / nch) * nch;
+    if (r < rows_valid && ch * 16 < col_bytes)
+      *(uint4 *)(dst + (size_t)r * ld + ch * 16) = *(const uint4 *)(plane + st_off(r, ch, nch));
+  }
+}
+
+// Copy rows from global memory (src, pitch ld bytes) into a plane; rows past
+// rows_valid or chunks past col_bytes are left unwritten.
+__device__ __forceinline__ void copy_rows_in(uint8_t *plane, int nch, int rows, int rows_valid,
+                                             int col_bytes, const uint8_t *src, long ld,
+                                             int tid) {
+  const int n = rows * nch;
+  for (int idx = tid; idx < n; idx += NT) {
+    const int r = idx / nch, ch = idx - (idx / nch) * nch;
+    if (r < rows_valid && ch * 16 < col_bytes)
+      *(uint4 *)(plane + st_off(r, ch, nch)) = *(const uint4 *)(src + (size_t)r * ld + ch * 16);
+  }
+}
+
+// Row (within its 128-row plane) of accumulator element v of 32-row block i.
+__device__ __forceinline__ int acc_row(int i, int v, int lane) {
+  return 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+// The wave's 128 x 128 accumulators as bf16 into its plane (512-byte rows).
+__device__ __forceinline__ void stage_acc_bf16(uint8_t *plane, const f32x16 (&acc)[4][4],
+                                               int wn0, int lane) {
+  const int ncol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++)
+        *(uint16_t *)(plane + st_byte(acc_row(i, v, lane), 2 * (wn0 + 32 * j + ncol), 32)) =
+            (uint16_t)f32_to_bf16(acc[i][j][v]);
+}
+
+// Tile geometry handed to the epilogues.
+struct TileAt {
+  int m0, n0, rowbase, Mg, wm0, wn0, lane, tid;
+};
+
+// Both planes' rows out to a row-major bf16 matrix C (pitch ldc elements),
+// columns from c0 (elements), `cols` valid columns of the tile.
+__device__ __forceinline__ void store_planes(uint8_t *L0, uint8_t *L1, int nch, const TileAt &t,
+                                             uint16_t *C, long ldc, long c0, int col_bytes) {
+#pragma unroll
+  for (int pl = 0; pl < 2; pl++) {
+    const int r0 = t.m0 + 128 * pl;
+    const int rv = min(128, t.Mg - r0);
+    if (rv > 0)
+      copy_rows_out(pl ? L1 : L0, nch, 128, rv, col_bytes,
+                    (uint8_t *)(C + (size_t)(t.rowbase + r0) * ldc + c0), ldc * 2, t.tid);
+  }
+}
+
+// EPI_BF16: C[rows][N] = bf16(acc).
+__device__ __forceinline__ void tile_epi_bf16(const GemmArgs &p, const f32x16 (&acc)[4][4],
+                                              uint8_t *L0, uint8_t *L1, const TileAt &t) {
+  __syncthreads();
+  stage_acc_bf16(t.wm0 ? L1 : L0, acc, t.wn0, t.lane);
+  __syncthreads();
+  store_planes(L0, L1, 32, t, (uint16_t *)p.C, p.ldc, t.n0, min(BN, p.N - t.n0) * 2);
+}
+
+// EPI_SWIGLU: packed columns hold 64-column blocks [32 gate | 32 up].
+// C2 (optional) <- g|u as bf16; C <- a = silu(g) u, as bf16, or with mx.q_out
+// quantised along I in 32-blocks (codes to q_out, scales to s_out, the round
+// trip as bf16 to C).
+template <bool MX>
+__device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOperands *mx,
+                                                const f32x16 (&acc)[4][4], uint8_t *L0,
+                                                uint8_t *L1, const TileAt &t) {
+  const int I = p.N / 2;
+  uint8_t *plane = t.wm0 ? L1 : L0;
+  __syncthreads();
+  if (p.C2) {
+    stage_acc_bf16(plane, acc, t.wn0, t.lane);
+    __syncthreads();
+    store_planes(L0, L1, 32, t, (uint16_t *)p.C2, p.ldc2, t.n0, min(BN, p.N - t.n0) * 2);
+    __syncthreads();
+  }
+  // a tile: 128 columns per row; plane layout [a bf16: 128 x 256 B][codes:
+  // 128 x 128 B][scales: 128 x 4 B]
+  const int ncol = t.lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++) {
+      const int ca = t.wn0 / 2 + 32 * jj + ncol;  // tile-local a column
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int r = acc_row(i, v, t.lane);
+        const float av = silu_f(acc[i][2 * jj][v]) * acc[i][2 * jj + 1][v];
+        if constexpr (!MX) {
+          *(uint16_t *)(plane + st_byte(r, 2 * ca, 16)) = (uint16_t)f32_to_bf16(av);
+        } else {
+          float amax = fabsf(av);
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          int s = -127;
+          if (amax > 0.0f) {
+            s = floor_log2(amax) - 8;
+            s = s < -127 ? -127 : (s > 127 ? 127 : s);
+          }
+          const float sc = fminf(fmaxf(ldexpf(av, -s), -448.0f), 448.0f);
+          const uint32_t code = amax > 0.0f ? e4m3_encode(sc, av < 0.0f) : 0u;
+          *(uint16_t *)(plane + st_byte(r, 2 * ca, 16)) =
+              (uint16_t)f32_to_bf16(ldexpf(e4m3_value(code), s));
+          plane[32768 + st_byte(r, ca, 8)] = (uint8_t)code;
+          if (ncol == 0) plane[49152 + r * 4 + (ca >> 5)] = (uint8_t)(s + 127);
+        }
+      }
+    }
+  __syncthreads();
+  const int a0 = t.n0 / 2, a_valid = min(BN / 2, I - a0);
+  store_planes(L0, L1, 16, t, (uint16_t *)p.C, p.ldc, a0, a_valid * 2);
+  if constexpr (MX) {
+#pragma unroll
+    for (int pl = 0; pl < 2; pl++) {
+      const int r0 = t.m0 + 128 * pl;
+      const int rv = min(128, t.Mg - r0);
+      if (rv <= 0) continue;
+      const uint8_t *src = pl ? L1 : L0;
+      const size_t row = (size_t)(t.rowbase + r0);
+      copy_rows_out(src + 32768, 8, 128, rv, a_valid, mx->q_out + row * I + a0, I, t.tid);
+      // scales: 4 bytes (the tile's four 32-blocks) per row
+      const int nb = (a_valid + 31) / 32;
+      for (int r = t.tid; r < rv; r += NT) {
+        uint8_t *d = mx->s_out + (row + r) * (I / 32) + a0 / 32;
+        if (nb == 4)
+          *(uint32_t *)d = *(const uint32_t *)(src + 49152 + r * 4);
+        else
+          for (int b = 0; b < nb; b++) d[b] = src[49152 + r * 4 + b];
+      }
+    }
+  }
+}
+
+// EPI_SWIGLU_BWD: the GEMM gives dA for intermediate columns; with the saved
+// g|u (p.aux, packed like the forward's C2) it writes dg|du (packed the same
+// way) to C:  dg = dA u silu'(g),  du = dA silu(g),
+// silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
+// The tile's 256 intermediate columns own a 512-column (1 KB) g|u span per
+// row; the 128 rows of one half of the tile fill both planes (rows 0-63 in
+// L0, 64-127 in L1), and the two waves that own those rows update them.
+template <int HALF>
+__device__ __forceinline__ void swiglu_bwd_half(const GemmArgs &p, const f32x16 (&acc)[4][4],
+                                                uint8_t *L0, uint8_t *L1, const TileAt &t) {
+  const int span_bytes = min(2 * BN, 2 * (p.N - t.n0)) * 2;  // valid bytes of the span
+  const long c0 = 2L * t.n0;                                // first packed column
+  const int r0 = t.m0 + 128 * HALF;
+  const int rv = min(128, t.Mg - r0);
+  __syncthreads();
+  if (rv > 0) {
+    const uint8_t *src = (const uint8_t *)(p.aux + (size_t)(t.rowbase + r0) * p.ldaux + c0);
+    copy_rows_in(L0, 64, 64, rv, span_bytes, src, p.ldaux * 2, t.tid);
+    if (rv > 64)
+      copy_rows_in(L1, 64, 64, rv - 64, span_bytes, src + (size_t)64 * p.ldaux * 2,
+                   p.ldaux * 2, t.tid);
+  }
+  __syncthreads();
+  if (rv > 0 && t.wm0 == 128 * HALF) {
+    const int ncol = t.lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint8_t *pl = i < 2 ? L0 : L1;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int c = t.wn0 + 32 * j + ncol;        // tile-local intermediate column
+        const int pg = (c >> 5) * 64 + (c & 31);    // its gate column in the span
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int r = acc_row(i, v, t.lane) & 63;
+          uint16_t *G = (uint16_t *)(pl + st_byte(r, 2 * pg, 64));
+          uint16_t *U = (uint16_t *)(pl + st_byte(r, 2 * (pg + 32), 64));
+          const float gv = bf16_to_f32(*G), uv = bf16_to_f32(*U);
+          const float dA = acc[i][j][v];
+          const float s = sigmoid_f(gv);
+          *G = (uint16_t)f32_to_bf16(dA * uv * s * (1.0f + gv * (1.0f - s)));
+          *U = (uint16_t)f32_to_bf16(dA * gv * s);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (rv > 0) {
+    uint8_t *dst = (uint8_t *)((uint16_t *)p.C + (size_t)(t.rowbase + r0) * p.ldc + c0);
+    copy_rows_out(L0, 64, 64, rv, span_bytes, dst, p.ldc * 2, t.tid);
+    if (rv > 64)
+      copy_rows_out(L1, 64, 64, rv - 64, span_bytes, dst + (size_t)64 * p.ldc * 2, p.ldc * 2,
+                    t.tid);
+  }
+}
+
+__device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
+                                                    const f32x16 (&acc)[4][4], uint8_t *L0,
+                                                    uint8_t *L1, const TileAt &t) {
+  swiglu_bwd_half<0>(p, acc, L0, L1, t);
+  swiglu_bwd_half<1>(p, acc, L0, L1, t);
+}
+
+}  // namespace moe
