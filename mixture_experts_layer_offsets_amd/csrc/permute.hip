@@ -22,42 +22,6 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// MXFP8 block conversion (E4M3 elements, E8M0 scale per 32 values):
-//   s = clamp(floor(log2 amax) - 8, -127, 127), scale code s + 127
-//   code_i = E4M3(clamp(v_i * 2^-s, -448, 448)), nearest-even;
-//   an all-zero block gets scale code 0.
-
-// Quantise 32 values; writes 32 codes (two uint4) and returns the scale code.
-// `deq` receives the dequantised values (may be null).
-__device__ __forceinline__ uint32_t mx_block(const float *v, uint4 *codes, float *deq) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-  int s = -127;
-  if (amax > 0.0f) {
-    s = floor_log2(amax) - 8;
-    s = s < -127 ? -127 : (s > 127 ? 127 : s);
-  }
-  uint32_t w[8];
-#pragma unroll
-  for (int q = 0; q < 8; q++) {
-    uint32_t d = 0;
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const float x = v[q * 4 + b];
-      const float sc = fminf(fmaxf(ldexpf(x, -s), -448.0f), 448.0f);
-      const uint32_t c = amax > 0.0f ? e4m3_encode(sc, x < 0.0f) : 0u;
-      d |= c << (8 * b);
-      if (deq) deq[q * 4 + b] = ldexpf(e4m3_value(c), s);
-    }
-    w[q] = d;
-  }
-  codes[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  codes[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  return (uint32_t)(s + 127);
-}
-
-// ---------------------------------------------------------------------------
 // Dispatch.  One wave per sorted row r copies token perm[r] / k.
 
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint4 *__restrict__ x,
@@ -78,49 +42,44 @@ void launch_dispatch_bf16(const uint16_t *x, const int32_t *perm, uint16_t *xp, 
                      (const uint4 *)x, perm, (uint4 *)xp, R, k, H / 8);
 }
 
-// MX dispatch: one thread per 32-element block of a row.  Writes the E4M3
-// codes, the E8M0 scales and (if xhat) the dequantised row as bf16.
+// MX dispatch: each lane converts 8 consecutive values (one 16-byte load),
+// four lanes of a quad form one 32-value block (block maximum by two DPP
+// exchanges), so loads and stores are contiguous across the wave.  Writes the
+// E4M3 codes, the E8M0 scales and (if xhat) the dequantised row as bf16.
+// The grid covers whole quads: R * H/8 is a multiple of 4.
 __global__ __launch_bounds__(256) void dispatch_mx_kernel(
-    const uint4 *__restrict__ x, const int32_t *__restrict__ perm, uint4 *__restrict__ xq,
-    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int R, int k, int NB /* H/32 */) {
+    const uint4 *__restrict__ x, const int32_t *__restrict__ perm, uint2 *__restrict__ xq,
+    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int R, int k, int HC /* H/8 */) {
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
-  if (id >= (long)R * NB) return;
-  const int r = (int)(id / NB), b = (int)(id - (long)r * NB);
+  if (id >= (long)R * HC) return;
+  const int r = (int)(id / HC), c = (int)(id - (long)r * HC);
   const int src_row = perm ? perm[r] / k : r;
-  const uint4 *src = x + (size_t)src_row * NB * 4 + b * 4;
-  float v[32];
-#pragma unroll
-  for (int q = 0; q < 4; q++) unpack8(src[q], v + 8 * q);
-  uint4 codes[2];
-  float deq[32];
-  const uint32_t sc = mx_block(v, codes, xhat ? deq : nullptr);
-  uint4 *dq = xq + (size_t)r * NB * 2 + b * 2;
-  dq[0] = codes[0];
-  dq[1] = codes[1];
-  xs[(size_t)r * NB + b] = (uint8_t)sc;
-  if (xhat) {
-    uint4 *dh = xhat + (size_t)r * NB * 4 + b * 4;
-#pragma unroll
-    for (int q = 0; q < 4; q++) dh[q] = pack8(deq + 8 * q);
-  }
+  float v[8];
+  unpack8(x[(size_t)src_row * HC + c], v);
+  uint2 codes;
+  float deq[8];
+  const uint32_t sc = mx_quad8(v, &codes, deq);
+  xq[(size_t)r * HC + c] = codes;
+  if ((c & 3) == 0) xs[(size_t)r * (HC / 4) + c / 4] = (uint8_t)sc;
+  if (xhat) xhat[(size_t)r * HC + c] = pack8(deq);
 }
 
 void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
                         uint16_t *xhat, int R, int k, int H, hipStream_t s) {
-  const long n = (long)R * (H / 32);
+  const long n = (long)R * (H / 8);
   if (n <= 0) return;
   hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const uint4 *)x, perm, (uint4 *)xq, xs, (uint4 *)xhat, R, k, H / 32);
+                     (const uint4 *)x, perm, (uint2 *)xq, xs, (uint4 *)xhat, R, k, H / 8);
 }
 
 // Row-wise MX quantisation of a bf16 matrix along its contiguous axis.
 void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
                           hipStream_t s) {
-  const long n = (long)rows * (cols / 32);
+  const long n = (long)rows * (cols / 8);
   if (n <= 0) return;
   hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const uint4 *)src, (const int32_t *)nullptr, (uint4 *)q, sc,
-                     (uint4 *)nullptr, rows, 1, cols / 32);
+                     (const uint4 *)src, (const int32_t *)nullptr, (uint2 *)q, sc,
+                     (uint4 *)nullptr, rows, 1, cols / 8);
 }
 
 // ---------------------------------------------------------------------------

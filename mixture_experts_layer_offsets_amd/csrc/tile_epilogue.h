@@ -104,9 +104,11 @@ __device__ __forceinline__ void tile_epi_bf16(const GemmArgs &p, const f32x16 (&
 }
 
 // EPI_SWIGLU: packed columns hold 64-column blocks [32 gate | 32 up].
-// C2 (optional) <- g|u as bf16; C <- a = silu(g) u, as bf16, or with mx.q_out
-// quantised along I in 32-blocks (codes to q_out, scales to s_out, the round
-// trip as bf16 to C).
+// C2 (optional) <- g|u as bf16; C <- a = silu(g) u as bf16, or with MX
+// (mx->q_out) a quantised along I in 32-blocks: codes to q_out, scales to
+// s_out, the round trip as bf16 to C.  For MX the tile's a values are staged
+// as fp32 (a plane row = 128 values = 512 bytes) and each thread then
+// converts whole 32-value blocks, so no cross-lane reduction is needed.
 template <bool MX>
 __device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOperands *mx,
                                                 const f32x16 (&acc)[4][4], uint8_t *L0,
@@ -120,8 +122,6 @@ __device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOpera
     store_planes(L0, L1, 32, t, (uint16_t *)p.C2, p.ldc2, t.n0, min(BN, p.N - t.n0) * 2);
     __syncthreads();
   }
-  // a tile: 128 columns per row; plane layout [a bf16: 128 x 256 B][codes:
-  // 128 x 128 B][scales: 128 x 4 B]
   const int ncol = t.lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -132,47 +132,43 @@ __device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOpera
       for (int v = 0; v < 16; v++) {
         const int r = acc_row(i, v, t.lane);
         const float av = silu_f(acc[i][2 * jj][v]) * acc[i][2 * jj + 1][v];
-        if constexpr (!MX) {
+        if constexpr (MX)
+          *(float *)(plane + st_byte(r, 4 * ca, 32)) = av;
+        else
           *(uint16_t *)(plane + st_byte(r, 2 * ca, 16)) = (uint16_t)f32_to_bf16(av);
-        } else {
-          float amax = fabsf(av);
-#pragma unroll
-          for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-          int s = -127;
-          if (amax > 0.0f) {
-            s = floor_log2(amax) - 8;
-            s = s < -127 ? -127 : (s > 127 ? 127 : s);
-          }
-          const float sc = fminf(fmaxf(ldexpf(av, -s), -448.0f), 448.0f);
-          const uint32_t code = amax > 0.0f ? e4m3_encode(sc, av < 0.0f) : 0u;
-          *(uint16_t *)(plane + st_byte(r, 2 * ca, 16)) =
-              (uint16_t)f32_to_bf16(ldexpf(e4m3_value(code), s));
-          plane[32768 + st_byte(r, ca, 8)] = (uint8_t)code;
-          if (ncol == 0) plane[49152 + r * 4 + (ca >> 5)] = (uint8_t)(s + 127);
-        }
       }
     }
   __syncthreads();
   const int a0 = t.n0 / 2, a_valid = min(BN / 2, I - a0);
-  store_planes(L0, L1, 16, t, (uint16_t *)p.C, p.ldc, a0, a_valid * 2);
-  if constexpr (MX) {
+  if constexpr (!MX) {
+    store_planes(L0, L1, 16, t, (uint16_t *)p.C, p.ldc, a0, a_valid * 2);
+  } else {
+    // 256 rows x 4 blocks of 32 values; 4 consecutive threads take one row
 #pragma unroll
-    for (int pl = 0; pl < 2; pl++) {
-      const int r0 = t.m0 + 128 * pl;
-      const int rv = min(128, t.Mg - r0);
-      if (rv <= 0) continue;
-      const uint8_t *src = pl ? L1 : L0;
-      const size_t row = (size_t)(t.rowbase + r0);
-      copy_rows_out(src + 32768, 8, 128, rv, a_valid, mx->q_out + row * I + a0, I, t.tid);
-      // scales: 4 bytes (the tile's four 32-blocks) per row
-      const int nb = (a_valid + 31) / 32;
-      for (int r = t.tid; r < rv; r += NT) {
-        uint8_t *d = mx->s_out + (row + r) * (I / 32) + a0 / 32;
-        if (nb == 4)
-          *(uint32_t *)d = *(const uint32_t *)(src + 49152 + r * 4);
-        else
-          for (int b = 0; b < nb; b++) d[b] = src[49152 + r * 4 + b];
+    for (int it = 0; it < 4; it++) {
+      const int q = t.tid + NT * it;
+      const int row = q >> 2, blk = q & 3;
+      const int grow_local = t.m0 + row;
+      if (grow_local >= t.Mg || blk * 32 >= a_valid) continue;
+      const uint8_t *pl = row < 128 ? L0 : L1;
+      const int r = row & 127;
+      float v[32];
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        const float4 f = *(const float4 *)(pl + st_off(r, blk * 8 + c, 32));
+        v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
       }
+      uint32_t w[8];
+      float deq[32];
+      const uint32_t sc = mx_block32(v, w, deq);
+      const size_t grow = (size_t)(t.rowbase + grow_local);
+      uint4 *dq = (uint4 *)(mx->q_out + grow * I + a0 + blk * 32);
+      dq[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dq[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      uint4 *dh = (uint4 *)((uint16_t *)p.C + grow * p.ldc + a0 + blk * 32);
+#pragma unroll
+      for (int c = 0; c < 4; c++) dh[c] = pack8(deq + 8 * c);
+      mx->s_out[grow * (I / 32) + a0 / 32 + blk] = (uint8_t)sc;
     }
   }
 }
