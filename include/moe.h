@@ -85,7 +85,9 @@ typedef struct moe_shape {
  * boundary i, for i < n_stage_events, so a caller can time each stage:
  *   forward : 0 start, 1 routing+layout done, 2 dispatch done, 3 gate/up
  *             GEMM + SwiGLU done, 4 down GEMM done, 5 shared expert done,
- *             6 combine done;
+ *             6 combine done (with use_megakernel, 2-5 are recorded when
+ *             the persistent kernel, which runs dispatch, both GEMMs, the
+ *             shared expert and combine together, has finished);
  *   backward: 0 start, 1 reverse-combine done, 2 down data-gradient GEMM
  *             (+ SwiGLU backward) done, 3 down weight-gradient GEMM done,
  *             4 gate/up data-gradient GEMM done, 5 gate/up weight-gradient
@@ -95,9 +97,14 @@ typedef struct moe_sched {
   int32_t minibatch_rows; /* routed rows per minibatch (0 = default) */
   int32_t ring_slots;     /* slots of the on-device ring (0 = default) */
   int32_t comm_cus;       /* CUs given to dispatch/combine (0 = default) */
-  int32_t use_megakernel; /* 0 = staged kernels, 1 = persistent pipelined kernel */
+  int32_t use_megakernel; /* 0 = staged kernels, 1 = persistent pipelined
+                             kernel (currently refused with
+                             MOE_ERR_UNSUPPORTED: switched off) */
   void **stage_events;    /* hipEvent_t[n_stage_events] or NULL */
   int32_t n_stage_events;
+  int32_t watchdog_us;    /* persistent kernel: microseconds one wait may take
+                             before it gives up and the layer reports
+                             MOE_ERR_DEVICE_TIMEOUT (0 = default, 2 s) */
 } moe_sched;
 
 /* ------------------------------------------------------------------ sizes */

@@ -5,7 +5,8 @@
 weights) as torch tensors and calls those entry points.  All computation is in
 libmoe's HIP kernels.
 """
-from ._lib import (MOE_BF16, MOE_MXFP8, MoeError, MoeSched, Shape, load,  # noqa: F401
+from ._lib import (MOE_BF16, MOE_ERR_DEVICE_TIMEOUT, MOE_MXFP8, MOE_OK, MoeError,  # noqa: F401
+                   MoeSched, Shape, load,
                    moe_combine, moe_dispatch, moe_expert_ffn, moe_layer_bwd, moe_layer_fwd,
                    moe_layout, moe_packed_weight_bytes, moe_prepare_weights, moe_read_status,
                    moe_route, moe_router_logits, moe_saved_bytes, moe_saved_pointers,

@@ -38,7 +38,8 @@ class MoeShape(ctypes.Structure):
 class MoeSched(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
                 ("comm_cus", ctypes.c_int32), ("use_megakernel", ctypes.c_int32),
-                ("stage_events", ctypes.POINTER(c_void_p)), ("n_stage_events", ctypes.c_int32)]
+                ("stage_events", ctypes.POINTER(c_void_p)), ("n_stage_events", ctypes.c_int32),
+                ("watchdog_us", ctypes.c_int32)]
 
 
 class MoeSavedView(ctypes.Structure):

@@ -27,7 +27,7 @@
 // about what a 256 x 256 bf16 tile consumes at full MFMA rate -- so the
 // kernels are co-limited by operand feed and matrix issue.
 #include "gemm_common.h"
-#include "tile_epilogue.h"
+#include "row_tile.h"
 
 namespace moe {
 
@@ -198,30 +198,17 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(GemmArgs p) {
 
 // ---------------------------------------------------------------------------
 // Row-ragged GEMM with both operands contraction-contiguous (the forward
-// gate/up and down GEMMs and both backward data-gradient GEMMs).
-//
-// Operands move from HBM straight into LDS with buffer_load_dwordx4 ... lds:
-// no staging registers and no ds_write instructions.  A wave's 16-byte load
-// lands lane-linearly in a 1 KB LDS segment (8 rows of 128 bytes), so each
-// lane fetches the global chunk that the XOR swizzle assigns to its LDS slot.
-// The buffer descriptor covers exactly the tile's valid rows: rows past the
-// end of the group read as zeros, with no per-row masks.  Two LDS buffers
-// (separate arrays, so the compiler can tell the one being filled from the
-// one being read) alternate per 64-deep K slice; MFMA fragments are double
-// buffered in registers so LDS latency hides behind the previous 16 MFMAs.
+// gate/up and down GEMMs and both backward data-gradient GEMMs); one tile per
+// workgroup, the tile itself in row_tile.h.
 
 template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t L0[2 * BM * BK];
   __shared__ __attribute__((aligned(1024))) uint16_t L1[2 * BM * BK];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
   const int MT = p.tile_start[p.G];
   const int nN = p.n_tiles_n;
-  const int total = MT * nN;
   const int b = blockIdx.x;
-  if (b >= total) return;
+  if (b >= MT * nN) return;
   // consecutive blocks share the A row tile (n fastest); measured faster on
   // this chip than XCD-grouped rasters for these shapes
   const int mt = b / nN, nt = b - (b / nN) * nN;
@@ -231,99 +218,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
     if (p.tile_start[mid] <= mt) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int m0 = (mt - p.tile_start[g]) * BM;
-  const int n0 = nt * BN;
   const int rowbase = p.offsets[g];
-  const int Mg = p.offsets[g + 1] - rowbase;
-  const int a_rows = min(BM, Mg - m0), b_rows = min(BN, p.N - n0);
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(p.A + (size_t)(rowbase + m0) * p.lda), (short)0, a_rows * (int)p.lda * 2,
-      kBufferDword3);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(p.B + (size_t)g * p.sB + (size_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb * 2,
-      kBufferDword3);
-  uint32_t oa[8], ob[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ swz5(row);
-    oa[i] = (uint32_t)(row * (int)p.lda * 2 + kc * 16);
-    ob[i] = (uint32_t)(row * (int)p.ldb * 2 + kc * 16);
-  }
-  auto issue = [&](uint16_t *L, int kt) {
-    const int soff = kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
-                                               oa[i], soff, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + BM * BK + (wave * 8 + i) * 512),
-                                               16, ob[i], soff, 0, 0);
-  };
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
-  const int fr = lane & 31;
-  const int cA = swz5(fr) ^ (lane >> 5);
-  const int baseA = (wm0 + fr) * BK, baseB = BM * BK + (wn0 + fr) * BK;
-  int offk[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ks++) offk[ks] = ((2 * ks) ^ cA) << 3;
-  auto compute = [&](const uint16_t *L) {
-    bf16x8 fa[2][4], fb[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      fa[0][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[0]);
-      fb[0][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[0]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-      const int c = ks & 1, nx = c ^ 1;
-      if (ks + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          fa[nx][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[ks + 1]);
-          fb[nx][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[ks + 1]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0,
-                                                              0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  const int nk = p.K / BK;
-  issue(L0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    issue(L1, kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(L0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < nk) issue(L0, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(L1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  if (kt < nk) compute(L0);
-  const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
-  if constexpr (EPI == EPI_BF16)
-    tile_epi_bf16(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
-  else if constexpr (EPI == EPI_SWIGLU)
-    tile_epi_swiglu<false>(p, nullptr, acc, (uint8_t *)L0, (uint8_t *)L1, t);
-  else
-    tile_epi_swiglu_bwd(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+  nt_tile<EPI>(p, g, (mt - p.tile_start[g]) * BM, nt * BN, rowbase, p.offsets[g + 1] - rowbase,
+               L0, L1);
 }
 
 template <bool WGRAD, bool B_KC>

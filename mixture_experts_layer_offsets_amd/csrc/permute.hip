@@ -18,6 +18,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mx_device.h"
+#include "rows.h"
 
 namespace moe {
 
@@ -86,30 +87,13 @@ void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, u
 // Combine + final weighted fusion: out[t] = sum_j w[t,j] y[inv[t*k+j]] (+ ys[t]),
 // fp32 fused multiply-adds in ascending j.  Grid (chunk groups, T).
 
-__global__ __launch_bounds__(128) void combine_kernel(const uint4 *__restrict__ y,
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t *__restrict__ y,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv,
-                                                      const uint4 *__restrict__ ys,
-                                                      uint4 *__restrict__ out, int k, int HC) {
-  const int t = blockIdx.y;
+                                                      const uint16_t *__restrict__ ys,
+                                                      uint16_t *__restrict__ out, int k, int HC) {
   const int c = blockIdx.x * 128 + threadIdx.x;
-  if (c >= HC) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; j++) {
-    const int f = t * k + j;
-    const float wj = w[f];
-    float v[8];
-    unpack8(y[(size_t)inv[f] * HC + c], v);
-#pragma unroll
-    for (int q = 0; q < 8; q++) acc[q] = fmaf(wj, v[q], acc[q]);
-  }
-  if (ys) {
-    float v[8];
-    unpack8(ys[(size_t)t * HC + c], v);
-#pragma unroll
-    for (int q = 0; q < 8; q++) acc[q] += v[q];
-  }
-  out[(size_t)t * HC + c] = pack8(acc);
+  if (c < HC) combine8(y, w, inv, ys, out, blockIdx.y, c, k, HC);
 }
 
 void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,
@@ -117,7 +101,7 @@ void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const
   const int HC = H / 8;
   if (T <= 0) return;
   hipLaunchKernelGGL(combine_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
-                     (const uint4 *)y, w, inv, (const uint4 *)ys, (uint4 *)out, k, HC);
+                     y, w, inv, ys, out, k, HC);
 }
 
 // ---------------------------------------------------------------------------

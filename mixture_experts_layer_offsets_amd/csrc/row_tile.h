@@ -1,0 +1,275 @@
+// One 256 x 256 output tile of a row-ragged grouped GEMM, as device
+// functions: the one-tile-per-workgroup kernels and the persistent layer
+// kernel both call them.
+#pragma once
+
+#include "gemm_common.h"
+#include "mx_device.h"
+#include "tile_epilogue.h"
+
+namespace moe {
+
+// Row-ragged GEMM with both operands contraction-contiguous (the forward
+// gate/up and down GEMMs and both backward data-gradient GEMMs).
+//
+// Operands move from HBM straight into LDS with buffer_load_dwordx4 ... lds:
+// no staging registers and no ds_write instructions.  A wave's 16-byte load
+// lands lane-linearly in a 1 KB LDS segment (8 rows of 128 bytes), so each
+// lane fetches the global chunk that the XOR swizzle assigns to its LDS slot.
+// The buffer descriptor covers exactly the tile's valid rows: rows past the
+// end of the group read as zeros, with no per-row masks.  Two LDS buffers
+// (separate arrays, so the compiler can tell the one being filled from the
+// one being read) alternate per 64-deep K slice; MFMA fragments are double
+// buffered in registers so LDS latency hides behind the previous 16 MFMAs.
+//
+// The tile covers rows [rowbase + m0, rowbase + min(m0 + 256, Mg)) of A and
+// the B matrix of group g; L0, L1 are the workgroup's two 64 KB LDS buffers.
+template <int EPI>
+__device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0, int rowbase,
+                                        int Mg, uint16_t *L0, uint16_t *L1) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int a_rows = min(BM, Mg - m0), b_rows = min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.A + (size_t)(rowbase + m0) * p.lda), (short)0, a_rows * (int)p.lda * 2,
+      kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.B + (size_t)g * p.sB + (size_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb * 2,
+      kBufferDword3);
+  uint32_t oa[8], ob[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz5(row);
+    oa[i] = (uint32_t)(row * (int)p.lda * 2 + kc * 16);
+    ob[i] = (uint32_t)(row * (int)p.ldb * 2 + kc * 16);
+  }
+  auto issue = [&](uint16_t *L, int kt) {
+    const int soff = kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
+                                               oa[i], soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + BM * BK + (wave * 8 + i) * 512),
+                                               16, ob[i], soff, 0, 0);
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+  const int fr = lane & 31;
+  const int cA = swz5(fr) ^ (lane >> 5);
+  const int baseA = (wm0 + fr) * BK, baseB = BM * BK + (wn0 + fr) * BK;
+  int offk[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) offk[ks] = ((2 * ks) ^ cA) << 3;
+  auto compute = [&](const uint16_t *L) {
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      fa[0][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[0]);
+      fb[0][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[0]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++) {
+      const int c = ks & 1, nx = c ^ 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          fa[nx][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[ks + 1]);
+          fb[nx][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[ks + 1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0,
+                                                              0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int nk = p.K / BK;
+  issue(L0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    issue(L1, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(L0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) issue(L0, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(L1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (kt < nk) compute(L0);
+  const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
+  if constexpr (EPI == EPI_BF16)
+    tile_epi_bf16(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+  else if constexpr (EPI == EPI_SWIGLU)
+    tile_epi_swiglu<false>(p, nullptr, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+  else
+    tile_epi_swiglu_bwd(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+}
+
+// Grouped GEMMs on MXFP8 operands (E4M3 codes with one E8M0 scale per 32
+// values along K) for the expert FFN's forward GEMMs and its backward data
+// gradients.  The pages fuse MXFP8 activation quantisation into the dispatch,
+// grouped-GEMM and SwiGLU data paths (kucoin.com news flash "O MoK do Cursor
+// alcança aumento de desempenho de 2,37x no NVIDIA GB300 NVL72", §02;
+// deepdigest.ru article on MoK).
+//
+// Same tile and operand feed as the bf16 kernel: 256 x 256 outputs per
+// 256-thread workgroup, four waves of 128 x 128, operands DMA'd into LDS in
+// 128-byte-deep stages (128 fp8 values per row), double buffered.  The matrix
+// instruction is v_mfma_scale_f32_32x32x64_f8f6f4: for a row (or column) of
+// the 32 x 64 operand, lane half h holds K bytes [16h, 16h+16) and
+// [32+16h, 32+16h+16), and the scale byte it supplies applies to the 32-wide
+// K block h (measured on MI355X).  Each fragment is therefore two 16-byte LDS
+// reads, and each lane reads one scale dword per 32-row block per stage.
+// The SwiGLU epilogue can quantise a = silu(g) * u along I (see
+// tile_epilogue.h).
+constexpr int MXK = 128;  // K bytes (= fp8 values) per stage
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The MXFP8 tile; same geometry and buffers as nt_tile.
+template <int EPI>
+__device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx, int g, int m0,
+                                        int n0, int rowbase, int Mg, uint8_t *L0, uint8_t *L1) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int a_rows = min(BM, Mg - m0), b_rows = min(BN, p.N - n0);
+  const int K = p.K, KS = K / 32;  // bytes per row of codes / of scales
+
+  const uint8_t *Ac = (const uint8_t *)p.A, *Bc = (const uint8_t *)p.B;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(Ac + (size_t)(rowbase + m0) * p.lda), (short)0, a_rows * (int)p.lda, kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(Bc + (size_t)g * p.sB + (size_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb,
+      kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rSa = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(mx.a_scale + (size_t)(rowbase + m0) * KS), (short)0, a_rows * KS, kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rSb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(mx.b_scale + (size_t)g * mx.sBs + (size_t)n0 * KS), (short)0, b_rows * KS,
+      kBufferDword3);
+
+  uint32_t oa[8], ob[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz5(row);
+    oa[i] = (uint32_t)(row * (int)p.lda + kc * 16);
+    ob[i] = (uint32_t)(row * (int)p.ldb + kc * 16);
+  }
+  auto issue = [&](uint8_t *L, int kt) {
+    const int soff = kt * MXK;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 1024), 16,
+                                               oa[i], soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + BM * MXK + (wave * 8 + i) * 1024),
+                                               16, ob[i], soff, 0, 0);
+  };
+  // scale dwords of this lane's rows: 4 blocks of 32 along K per stage
+  const int fr = lane & 31, h = lane >> 5;
+  auto load_scales = [&](int kt, int *sa, int *sb) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sa[i] = __builtin_amdgcn_raw_buffer_load_b32(rSa, (wm0 + 32 * i + fr) * KS + kt * 4, 0, 0);
+      sb[i] = __builtin_amdgcn_raw_buffer_load_b32(rSb, (wn0 + 32 * i + fr) * KS + kt * 4, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+
+  const int sw = swz5(fr);
+  const int baseA = (wm0 + fr) * MXK, baseB = BM * MXK + (wn0 + fr) * MXK;
+  auto compute = [&](const uint8_t *L, const int *sa, const int *sb) {
+    i32x8 fa[2][4], fb[2][4];
+    auto load = [&](int ks, int set) {
+      const int c0 = ((4 * ks + h) ^ sw) << 4, c1 = ((4 * ks + 2 + h) ^ sw) << 4;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint4 x0 = *(const uint4 *)(L + baseA + i * 32 * MXK + c0);
+        const uint4 x1 = *(const uint4 *)(L + baseA + i * 32 * MXK + c1);
+        fa[set][i] = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                             (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        const uint4 y0 = *(const uint4 *)(L + baseB + i * 32 * MXK + c0);
+        const uint4 y1 = *(const uint4 *)(L + baseB + i * 32 * MXK + c1);
+        fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                             (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+      }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      if (ks == 0) load(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int sh = 8 * (2 * ks + h);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0, (sa[i] >> sh) & 0xFF, 0,
+              (sb[j] >> sh) & 0xFF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int nk = K / MXK;
+  int sa0[4], sb0[4], sa1[4], sb1[4];
+  issue(L0, 0);
+  load_scales(0, sa0, sb0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    issue(L1, kt + 1);
+    load_scales(kt + 1, sa1, sb1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(L0, sa0, sb0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) {
+      issue(L0, kt + 2);
+      load_scales(kt + 2, sa0, sb0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(L1, sa1, sb1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (kt < nk) compute(L0, sa0, sb0);
+
+  const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
+  if constexpr (EPI == EPI_BF16) {
+    tile_epi_bf16(p, acc, L0, L1, t);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (mx.q_out)
+      tile_epi_swiglu<true>(p, &mx, acc, L0, L1, t);
+    else
+      tile_epi_swiglu<false>(p, nullptr, acc, L0, L1, t);
+  } else {
+    tile_epi_swiglu_bwd(p, acc, L0, L1, t);
+  }
+}
+
+}  // namespace moe

@@ -142,3 +142,14 @@ def test_mx_sizes_and_shape_rules(lib):
         assert m.moe_workspace_bytes(bad) == 0
         assert lib.moe_route(ctypes.byref(bad.c()), 1 << 40, 1 << 40, 1 << 40, None) == \
             _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_megakernel_request_is_refused(lib):
+    """The persistent forward is switched off: asking for it returns
+    MOE_ERR_UNSUPPORTED before any device work."""
+    s = ctypes.byref(m.Shape(64, 128, 8, 2, 64).c())
+    sched = m.MoeSched()
+    sched.use_megakernel = 1
+    fake = 1 << 40
+    assert lib.moe_layer_fwd(s, ctypes.byref(sched), fake, None, None, fake, fake, fake, fake,
+                             fake, fake, 1 << 40, None) == _lib.MOE_ERR_UNSUPPORTED
