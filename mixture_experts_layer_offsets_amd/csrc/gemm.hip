@@ -223,6 +223,142 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
                L0, L1);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-gradient GEMM with both operands row-major over the contraction:
+// C_g[M][N] = sum over the group's rows r of A[r][M]^T B[r][N].
+//
+// The 64-row K slices of A and B (rows of 256 M or N values, 512 bytes) move
+// into LDS untransposed by direct-to-LDS DMA, exactly as they lie in HBM; the
+// buffer descriptor starts at the group's first row and ends at its last, so
+// the ragged K tail reads zeros.  The MFMA fragments (8 consecutive k of one
+// m per lane) are then read with ds_read_b64_tr_b16, gfx950's transposing LDS
+// read: within each 16-lane group, output lane 4a + b receives element b of
+// the 4-element chunks addressed by lanes a, 4 + a, 8 + a and 12 + a
+// (measured on MI355X).  Lane j of a group therefore addresses row
+// k0 + j/4 at column base + 4 (j % 4), and two such reads (k0, k0 + 4) give
+// a lane its 8 k values.  16-byte chunks are XOR-swizzled by 4 (k & 3) so the
+// four rows one read touches land in four different bank groups.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 *lds_v4i16_t;
+
+__device__ __forceinline__ int tn_swz(int k) { return (k & 3) << 2; }
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t L0[2 * 64 * BM];  // [A | B], even stages
+  __shared__ __attribute__((aligned(1024))) uint16_t L1[2 * 64 * BM];  // [A | B], odd stages
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int per = p.n_tiles_m * p.n_tiles_n;
+  const int gi = blockIdx.x / per;
+  const int rem = blockIdx.x - gi * per;
+  const int g = p.order ? p.order[gi] : gi;
+  const int mt = rem / p.n_tiles_n;
+  const int m0 = mt * BM, n0 = (rem - mt * p.n_tiles_n) * BN;
+  const int koff = p.offsets[g];
+  const int Kg = p.offsets[g + 1] - koff;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+
+  if (Kg > 0) {
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.A + (size_t)koff * p.lda + m0), (short)0, Kg * (int)p.lda * 2, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.B + (size_t)koff * p.ldb + n0), (short)0, Kg * (int)p.ldb * 2, kBufferDword3);
+    // DMA: instruction i of wave w fills LDS rows 2 (8w + i) + {0, 1}; lane L
+    // writes chunk L % 32 of row 2 (8w + i) + L / 32 and so fetches the global
+    // chunk that the swizzle maps there.
+    uint32_t oa[8], ob[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int row = 2 * (wave * 8 + i) + (lane >> 5);
+      const int c = (lane & 31) ^ tn_swz(row);
+      oa[i] = (uint32_t)(row * (int)p.lda * 2 + c * 16);
+      ob[i] = (uint32_t)(row * (int)p.ldb * 2 + c * 16);
+    }
+    auto issue = [&](uint16_t *L, int kt) {
+      const int sa = kt * 64 * (int)p.lda * 2, sb = kt * 64 * (int)p.ldb * 2;
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
+                                                 oa[i], sa, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + 64 * BM + (wave * 8 + i) * 512),
+                                                 16, ob[i], sb, 0, 0);
+    };
+    // fragment addresses: lane l in 16-lane group q = l / 16, j = l % 16
+    const int q = lane >> 4, j = lane & 15;
+    const int krow = 8 * (q >> 1) + (j >> 2);          // + 16 ks + {0, 4}
+    const int colA = wm0 + 16 * (q & 1) + 4 * (j & 3);  // + 32 i
+    const int colB = wn0 + 16 * (q & 1) + 4 * (j & 3);  // + 32 i
+    // element offset of (row k, column c) in an operand slice
+    auto off = [](int k, int c) { return k * BM + (((c >> 3) ^ tn_swz(k)) << 3) + (c & 7); };
+    auto frag = [&](const uint16_t *T, int k0, int c) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(T + off(k0, c)));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(T + off(k0 + 4, c)));
+      bf16x8 f;
+      const v4i16 *plo = &lo, *phi = &hi;
+      __builtin_memcpy(&f, plo, 8);
+      __builtin_memcpy((char *)&f + 8, phi, 8);
+      return f;
+    };
+    auto compute = [&](const uint16_t *L) {
+      const uint16_t *TA = L, *TB = L + 64 * BM;
+      bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        fa[0][i] = frag(TA, krow, colA + 32 * i);
+        fb[0][i] = frag(TB, krow, colB + 32 * i);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) {
+        const int c = ks & 1, nx = c ^ 1;
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            fa[nx][i] = frag(TA, 16 * (ks + 1) + krow, colA + 32 * i);
+            fb[nx][i] = frag(TB, 16 * (ks + 1) + krow, colB + 32 * i);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj],
+                                                                 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    const int nk = (Kg + 63) / 64;
+    issue(L0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      issue(L1, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(L0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 2 < nk) issue(L0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(L1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (kt < nk) compute(L0);
+  }
+  epilogue<true, EPI>(p, acc, g, m0, n0, 0, p.M, wm0, wn0, lane);
+}
+
 template <bool WGRAD, bool B_KC>
 static void launch_epi(const GemmArgs &p, int epi, int grid, hipStream_t s) {
   const dim3 g(grid), b(NT);
@@ -261,6 +397,15 @@ void launch_gemm_wgrad(const GemmArgs &p0, int epi, hipStream_t s) {
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long grid = (long)p.G * p.n_tiles_m * p.n_tiles_n;
   if (grid <= 0) return;
+  if (p.lda % 8 == 0 && p.ldb % 8 == 0 && p.lda >= BM && p.ldb >= BN &&
+      (epi == EPI_F32 || epi == EPI_WGRAD_GU)) {
+    const dim3 gr((unsigned)grid), b(NT);
+    if (epi == EPI_F32)
+      hipLaunchKernelGGL(gemm_tn_kernel<EPI_F32>, gr, b, 0, s, p);
+    else
+      hipLaunchKernelGGL(gemm_tn_kernel<EPI_WGRAD_GU>, gr, b, 0, s, p);
+    return;
+  }
   launch_epi<true, false>(p, epi, (int)grid, s);
 }
 
