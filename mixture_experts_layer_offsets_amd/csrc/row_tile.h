@@ -67,51 +67,58 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
   int offk[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ks++) offk[ks] = ((2 * ks) ^ cA) << 3;
-  auto compute = [&](const uint16_t *L) {
-    bf16x8 fa[2][4], fb[2][4];
+  // Fragments double-buffered across the whole K loop: in each stage, the
+  // wait for the next stage's operands and the barrier come after the third
+  // k-slice's MFMAs are issued (they keep the matrix pipe busy meanwhile),
+  // and the next stage's first fragments load while the last slice's MFMAs
+  // run.  Set s & 1 holds the fragments of k-slice s of a stage.
+  bf16x8 fa[2][4], fb[2][4];
+  auto load = [&](const uint16_t *L, int ks, int set) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      fa[0][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[0]);
-      fb[0][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[0]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-      const int c = ks & 1, nx = c ^ 1;
-      if (ks + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          fa[nx][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[ks + 1]);
-          fb[nx][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[ks + 1]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0,
-                                                              0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      fa[set][i] = *(const bf16x8 *)(L + baseA + i * 32 * BK + offk[ks]);
+      fb[set][i] = *(const bf16x8 *)(L + baseB + i * 32 * BK + offk[ks]);
     }
   };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0,
+                                                            0, 0);
+  };
   const int nk = p.K / BK;
+  // Lc holds stage kt, Ln receives stage kt + 1 (in flight); Lc is refilled
+  // with stage kt + 2 once every wave has its last fragments of stage kt.
+  auto stage = [&](uint16_t *Lc, const uint16_t *Ln, int kt) {
+#pragma unroll
+    for (int ks = 0; ks < 3; ks++) {
+      load(Lc, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) issue(Lc, kt + 2);
+    load(Ln, 0, 0);  // after the last stage this reads a stale buffer, unused
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   issue(L0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (nk > 1) issue(L1, 1);
+  load(L0, 0, 0);
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    issue(L1, kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(L0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < nk) issue(L0, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(L1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  for (; kt + 2 <= nk; kt += 2) {
+    stage(L0, L1, kt);
+    stage(L1, L0, kt + 1);
   }
-  if (kt < nk) compute(L0);
+  if (kt < nk) stage(L0, L1, kt);
+  __syncthreads();  // the epilogue reuses both buffers
   const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
   if constexpr (EPI == EPI_BF16)
     tile_epi_bf16(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
