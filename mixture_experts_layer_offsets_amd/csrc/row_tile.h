@@ -147,6 +147,11 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
 // tile_epilogue.h).
 constexpr int MXK = 128;  // K bytes (= fp8 values) per stage
 
+// s_waitcnt vmcnt(0) with the other counters left alone, as the builtin (the
+// compiler's own wait insertion sees it, unlike inline asm, and so knows the
+// scale dwords loaded before it have arrived).
+constexpr int kVmcnt0 = 0x0F70;
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // The MXFP8 tile; same geometry and buffers as nt_tile.
@@ -179,15 +184,23 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
     oa[i] = (uint32_t)(row * (int)p.lda + kc * 16);
     ob[i] = (uint32_t)(row * (int)p.ldb + kc * 16);
   }
+  // A stage index past the end selects empty descriptors: the DMA then writes
+  // zeros into the (no longer read) buffer and touches no memory.  This keeps
+  // the main loop free of branches, which would let the compiler sink the
+  // MFMAs of a k-slice past the barrier and collapse the pipeline.
+  const __amdgpu_buffer_rsrc_t rNone =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Ac, (short)0, 0, kBufferDword3);
   auto issue = [&](uint8_t *L, int kt) {
-    const int soff = kt * MXK;
+    const bool live = kt < K / MXK;
+    const __amdgpu_buffer_rsrc_t ra = live ? rA : rNone, rb = live ? rB : rNone;
+    const int soff = live ? kt * MXK : 0;
 #pragma unroll
     for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(L + (wave * 8 + i) * 1024), 16,
                                                oa[i], soff, 0, 0);
 #pragma unroll
     for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + BM * MXK + (wave * 8 + i) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(L + BM * MXK + (wave * 8 + i) * 1024),
                                                16, ob[i], soff, 0, 0);
   };
   // scale dwords of this lane's rows: 4 blocks of 32 along K per stage
@@ -208,63 +221,71 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
 
   const int sw = swz5(fr);
   const int baseA = (wm0 + fr) * MXK, baseB = BM * MXK + (wn0 + fr) * MXK;
-  auto compute = [&](const uint8_t *L, const int *sa, const int *sb) {
-    i32x8 fa[2][4], fb[2][4];
-    auto load = [&](int ks, int set) {
-      const int c0 = ((4 * ks + h) ^ sw) << 4, c1 = ((4 * ks + 2 + h) ^ sw) << 4;
+  // Same pipeline as nt_tile, with two 64-deep k-slices per stage: slice 1's
+  // fragments load while slice 0's MFMAs run, then the wait and the barrier,
+  // then the next stage's slice-0 fragments load while slice 1's MFMAs run.
+  // Scale dwords for stage kt + 2 are fetched after slice 1's MFMAs are
+  // issued (they reuse stage kt's registers) and arrive by the next wait.
+  i32x8 fa[2][4], fb[2][4];
+  auto load = [&](const uint8_t *L, int ks, int set) {
+    const int c0 = ((4 * ks + h) ^ sw) << 4, c1 = ((4 * ks + 2 + h) ^ sw) << 4;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const uint4 x0 = *(const uint4 *)(L + baseA + i * 32 * MXK + c0);
-        const uint4 x1 = *(const uint4 *)(L + baseA + i * 32 * MXK + c1);
-        fa[set][i] = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                             (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        const uint4 y0 = *(const uint4 *)(L + baseB + i * 32 * MXK + c0);
-        const uint4 y1 = *(const uint4 *)(L + baseB + i * 32 * MXK + c1);
-        fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
-                             (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
-      }
-    };
-    load(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      if (ks == 0) load(1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      const int sh = 8 * (2 * ks + h);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0, (sa[i] >> sh) & 0xFF, 0,
-              (sb[j] >> sh) & 0xFF);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 4; i++) {
+      const uint4 x0 = *(const uint4 *)(L + baseA + i * 32 * MXK + c0);
+      const uint4 x1 = *(const uint4 *)(L + baseA + i * 32 * MXK + c1);
+      fa[set][i] = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                           (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      const uint4 y0 = *(const uint4 *)(L + baseB + i * 32 * MXK + c0);
+      const uint4 y1 = *(const uint4 *)(L + baseB + i * 32 * MXK + c1);
+      fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                           (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
     }
+  };
+  auto mma = [&](int ks, const int *sa, const int *sb) {
+    const int sh = 8 * (2 * ks + h);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0, (sa[i] >> sh) & 0xFF, 0,
+            (sb[j] >> sh) & 0xFF);
   };
 
   const int nk = K / MXK;
   int sa0[4], sb0[4], sa1[4], sb1[4];
+  // Lc holds stage kt (scales sa, sb), Ln receives stage kt + 1.
+  auto stage = [&](uint8_t *Lc, const uint8_t *Ln, int kt, int *sa, int *sb) {
+    load(Lc, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, sa, sb);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    issue(Lc, kt + 2);  // zeros past the end
+    load(Ln, 0, 0);     // after the last stage this reads zeros, unused
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, sa, sb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_scales(min(kt + 2, nk - 1), sa, sb);
+  };
   issue(L0, 0);
   load_scales(0, sa0, sb0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    issue(L1, kt + 1);
-    load_scales(kt + 1, sa1, sb1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(L0, sa0, sb0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < nk) {
-      issue(L0, kt + 2);
-      load_scales(kt + 2, sa0, sb0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(L1, sa1, sb1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  if (nk > 1) {
+    issue(L1, 1);
+    load_scales(1, sa1, sb1);
   }
-  if (kt < nk) compute(L0, sa0, sb0);
+  load(L0, 0, 0);
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    stage(L0, L1, kt, sa0, sb0);
+    stage(L1, L0, kt + 1, sa1, sb1);
+  }
+  if (kt < nk) stage(L0, L1, kt, sa0, sb0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
+  __syncthreads();  // the epilogue reuses both buffers
 
   const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
   if constexpr (EPI == EPI_BF16) {
