@@ -111,6 +111,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, f32x16 (&acc)[4][4],
 
 constexpr uint32_t kBufferDword3 = 0x00020000;  // raw buffer, gfx9 family
 
+// s_waitcnt vmcnt(0) with the other counters left alone, issued through the
+// builtin: the compiler's own wait insertion sees it (inline asm it does not)
+// and so knows that every vector-memory load issued before it has arrived.
+constexpr int kVmcnt0 = 0x0F70;
+
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // Chunk swizzle of the DMA-fed tiles (rows of 64 bf16 = eight 16-byte

@@ -45,15 +45,23 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
     oa[i] = (uint32_t)(row * (int)p.lda * 2 + kc * 16);
     ob[i] = (uint32_t)(row * (int)p.ldb * 2 + kc * 16);
   }
+  // A stage index past the end selects empty descriptors: the DMA then writes
+  // zeros into the (no longer read) buffer and touches no memory.  This keeps
+  // the K loop free of branches, across which the compiler could otherwise
+  // sink a k-slice's MFMAs past the barrier.
+  const __amdgpu_buffer_rsrc_t rNone =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, 0, kBufferDword3);
   auto issue = [&](uint16_t *L, int kt) {
-    const int soff = kt * BK * 2;
+    const bool live = kt < p.K / BK;
+    const __amdgpu_buffer_rsrc_t ra = live ? rA : rNone, rb = live ? rB : rNone;
+    const int soff = live ? kt * BK * 2 : 0;
 #pragma unroll
     for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
                                                oa[i], soff, 0, 0);
 #pragma unroll
     for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + BM * BK + (wave * 8 + i) * 512),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(L + BM * BK + (wave * 8 + i) * 512),
                                                16, ob[i], soff, 0, 0);
   };
   f32x16 acc[4][4];
@@ -99,18 +107,18 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
       mma(ks & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (kt + 2 < nk) issue(Lc, kt + 2);
-    load(Ln, 0, 0);  // after the last stage this reads a stale buffer, unused
+    issue(Lc, kt + 2);  // zeros past the end
+    load(Ln, 0, 0);     // after the last stage this reads zeros, unused
     __builtin_amdgcn_sched_barrier(0);
     mma(1);
     __builtin_amdgcn_sched_barrier(0);
   };
   issue(L0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  if (nk > 1) issue(L1, 1);
+  issue(L1, 1);
   load(L0, 0, 0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
@@ -118,7 +126,8 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
     stage(L1, L0, kt + 1);
   }
   if (kt < nk) stage(L0, L1, kt);
-  __syncthreads();  // the epilogue reuses both buffers
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
+  __syncthreads();                      // the epilogue reuses both buffers
   const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
   if constexpr (EPI == EPI_BF16)
     tile_epi_bf16(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
@@ -146,11 +155,6 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
 // The SwiGLU epilogue can quantise a = silu(g) * u along I (see
 // tile_epilogue.h).
 constexpr int MXK = 128;  // K bytes (= fp8 values) per stage
-
-// s_waitcnt vmcnt(0) with the other counters left alone, as the builtin (the
-// compiler's own wait insertion sees it, unlike inline asm, and so knows the
-// scale dwords loaded before it have arrived).
-constexpr int kVmcnt0 = 0x0F70;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -273,10 +277,8 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   load_scales(0, sa0, sb0);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  if (nk > 1) {
-    issue(L1, 1);
-    load_scales(1, sa1, sb1);
-  }
+  issue(L1, 1);
+  load_scales(min(1, nk - 1), sa1, sb1);
   load(L0, 0, 0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
