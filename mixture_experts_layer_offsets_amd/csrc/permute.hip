@@ -23,7 +23,12 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Dispatch.  One wave per sorted row r copies token perm[r] / k.
+// Dispatch.  One wave per sorted row r copies token perm[r] / k.  Each lane
+// issues up to kCopyBatch 16-byte loads before its first store, so a wave
+// keeps a whole batch of the row in flight instead of one chunk per memory
+// round trip.
+
+constexpr int kCopyBatch = 8;
 
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint4 *__restrict__ x,
                                                             const int32_t *__restrict__ perm,
@@ -33,7 +38,21 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint4 *__restr
   if (r >= R) return;
   const uint4 *src = x + (size_t)(perm[r] / k) * HC;
   uint4 *dst = xp + (size_t)r * HC;
-  for (int c = threadIdx.x & 63; c < HC; c += 64) dst[c] = src[c];
+  for (int c0 = threadIdx.x & 63; c0 < HC; c0 += 64 * kCopyBatch) {
+    // loads past the row's end re-read its last chunk (kept in registers,
+    // not stored), so the batch needs no predicated loads
+    uint4 v[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; u++) v[u] = src[min(c0 + 64 * u, HC - 1)];
+    // the values are needed here, so the compiler cannot sink each load into
+    // its (predicated) store's block, one round trip per chunk
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; u++)
+      asm volatile("" ::"v"(v[u].x), "v"(v[u].y), "v"(v[u].z), "v"(v[u].w));
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; u++)
+      if (c0 + 64 * u < HC) dst[c0 + 64 * u] = v[u];
+  }
 }
 
 void launch_dispatch_bf16(const uint16_t *x, const int32_t *perm, uint16_t *xp, int R, int k,
@@ -124,26 +143,45 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
   int rows[kMaxTopK];
   float wt[kMaxTopK];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) {
-    rows[j] = j < k ? inv[t * k + j] : 0;
-    wt[j] = j < k ? w[t * k + j] : 0.0f;
+  for (int j = 0; j < kMaxTopK; j++) {  // slots past k repeat the last one, unused
+    rows[j] = inv[t * k + min(j, k - 1)];
+    wt[j] = w[t * k + min(j, k - 1)];
   }
-  for (int c = tid; c < HC; c += 256) {
-    float d[8];
-    unpack8(dout[(size_t)t * HC + c], d);
+  // Two chunks per lane per pass, all of a pass's loads issued before its
+  // arithmetic; partial dot products still accumulate chunk by chunk in
+  // ascending column order.
+  for (int c0 = tid; c0 < HC; c0 += 512) {
+    const bool has1 = c0 + 256 < HC;
+    const uint4 d0 = dout[(size_t)t * HC + c0];
+    const uint4 d1 = has1 ? dout[(size_t)t * HC + c0 + 256] : make_uint4(0, 0, 0, 0);
+    uint4 yv[kMaxTopK][2];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; j++) {
       if (j < k) {
-        float v[8], o[8];
-        unpack8(y[(size_t)rows[j] * HC + c], v);
-        float s = 0.0f;
+        yv[j][0] = y[(size_t)rows[j] * HC + c0];
+        if (has1) yv[j][1] = y[(size_t)rows[j] * HC + c0 + 256];
+      }
+    }
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-          s = fmaf(d[q], v[q], s);
-          o[q] = wt[j] * d[q];
+    for (int u = 0; u < 2; u++) {
+      if (u == 1 && !has1) break;
+      const int c = c0 + 256 * u;
+      float d[8];
+      unpack8(u ? d1 : d0, d);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; j++) {
+        if (j < k) {
+          float v[8], o[8];
+          unpack8(yv[j][u], v);
+          float s = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; q++) {
+            s = fmaf(d[q], v[q], s);
+            o[q] = wt[j] * d[q];
+          }
+          part[j] += s;
+          dy[(size_t)rows[j] * HC + c] = pack8(o);
         }
-        part[j] += s;
-        dy[(size_t)rows[j] * HC + c] = pack8(o);
       }
     }
   }
@@ -185,12 +223,26 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
   const int t = blockIdx.y;
   const int c = blockIdx.x * 128 + threadIdx.x;
   if (c >= HC) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; j++) {
-    float v[8];
-    unpack8(dX[(size_t)inv[t * k + j] * HC + c], v);
+  // all k row indices, then all k rows' chunks, in flight before the first
+  // add (index slots past k repeat the last one)
+  int row[kMaxTopK];
 #pragma unroll
-    for (int q = 0; q < 8; q++) acc[q] += v[q];
+  for (int j = 0; j < kMaxTopK; j++) row[j] = inv[t * k + min(j, k - 1)];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; j++) asm volatile("" ::"v"(row[j]));  // materialise here
+  uint4 rv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; j++)
+    if (j < k) rv[j] = dX[(size_t)row[j] * HC + c];
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; j++) {
+    if (j < k) {
+      float v[8];
+      unpack8(rv[j], v);
+#pragma unroll
+      for (int q = 0; q < 8; q++) acc[q] += v[q];
+    }
   }
   if (wrT) {
     for (int j = 0; j < k; j++) {

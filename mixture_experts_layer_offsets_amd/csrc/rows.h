@@ -5,20 +5,42 @@
 
 namespace moe {
 
+constexpr int kCombineMaxK = 16;  // top-k bound of the library
+
 // Combine + final weighted fusion of 8 columns (16-byte chunk c) of token t:
 // out[t] = sum_j w[t,j] y[inv[t*k+j]] (+ ys[t]), fp32 fused multiply-adds in
-// ascending j, rounded to bf16 once.
+// ascending j, rounded to bf16 once.  All k rows' chunks are loaded before
+// the first multiply-add, so one memory round trip covers the token.
 __device__ __forceinline__ void combine8(const uint16_t *y, const float *w, const int32_t *inv,
                                          const uint16_t *ys, uint16_t *out, int t, int c, int k,
                                          int HC) {
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; j++) {
-    const int f = t * k + j;
-    const float wj = w[f];
-    float v[8];
-    unpack8(((const uint4 *)y)[(size_t)inv[f] * HC + c], v);
+  // row indices and weights first, unconditionally (slots past k repeat the
+  // last one), so their loads issue together rather than one per row load
+  int row[kCombineMaxK];
+  float wt[kCombineMaxK];
 #pragma unroll
-    for (int q = 0; q < 8; q++) acc[q] = fmaf(wj, v[q], acc[q]);
+  for (int j = 0; j < kCombineMaxK; j++) {
+    row[j] = inv[t * k + min(j, k - 1)];
+    wt[j] = w[t * k + min(j, k - 1)];
+  }
+  // (needed here: keeps the compiler from sinking each index load next to
+  // its row load)
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; j++) asm volatile("" ::"v"(row[j]));
+  uint4 rv[kCombineMaxK];
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; j++)
+    if (j < k) rv[j] = ((const uint4 *)y)[(size_t)row[j] * HC + c];
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; j++) {
+    if (j < k) {
+      const float wj = wt[j];
+      float v[8];
+      unpack8(rv[j], v);
+#pragma unroll
+      for (int q = 0; q < 8; q++) acc[q] = fmaf(wj, v[q], acc[q]);
+    }
   }
   if (ys) {
     float v[8];
