@@ -681,12 +681,12 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
     for (int i = 2; i <= 6; i++) st.mark(i);
     return hip_status();
   }
-  // Dispatch (MXFP8: quantised while gathered; the round trip is kept for the
-  // weight gradients)
+  // Dispatch, token-driven (MXFP8: each token quantised once; the round trip
+  // is kept for the weight gradients)
   if (d.mx)
-    launch_dispatch_mx(x, sv.perm, sv.xq.q, sv.xq.s, sv.x_perm, (int)d.R, k, H, s);
+    launch_dispatch_push_mx(x, sv.inv, sv.xq.q, sv.xq.s, sv.x_perm, T, k, H, s);
   else
-    launch_dispatch_bf16(x, sv.perm, sv.x_perm, (int)d.R, k, H, s);
+    launch_dispatch_push_bf16(x, sv.inv, sv.x_perm, T, k, H, s);
   st.mark(2);
   // Expert FFN
   ffn_forward(sv.x_perm, sv.xq, sv.offsets, sv.tile_start, E, d.R, d.H, d.I, p.r, d.mx, sv.act,

@@ -29,6 +29,11 @@ void launch_dispatch_bf16(const uint16_t *x, const int32_t *perm, uint16_t *xp, 
                           int H, hipStream_t s);
 void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
                         uint16_t *xhat, int R, int k, int H, hipStream_t s);
+// Scatter forms (token-driven, need inv = perm^-1): same outputs as above.
+void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T, int k,
+                               int H, hipStream_t s);
+void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq, uint8_t *xs,
+                             uint16_t *xhat, int T, int k, int H, hipStream_t s);
 void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
                           hipStream_t s);
 void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,

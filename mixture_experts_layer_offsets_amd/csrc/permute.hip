@@ -29,6 +29,7 @@ namespace moe {
 // round trip.
 
 constexpr int kCopyBatch = 8;
+constexpr int kMaxTopKPush = 16;  // top-k bound of the library
 
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint4 *__restrict__ x,
                                                             const int32_t *__restrict__ perm,
@@ -90,6 +91,71 @@ void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uin
   if (n <= 0) return;
   hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      (const uint4 *)x, perm, (uint2 *)xq, xs, (uint4 *)xhat, R, k, H / 8);
+}
+
+// Dispatch in scatter form, for the layer (which has inv = perm^-1): token
+// t's row is read -- and with MXFP8 quantised -- once, then written to its k
+// sorted rows inv[t*k + j].  Same result as the gather above; it reads each
+// token once instead of k times.  Grid (H/8 chunks over 128 threads, T).
+
+__global__ __launch_bounds__(128) void dispatch_push_bf16_kernel(const uint4 *__restrict__ x,
+                                                                 const int32_t *__restrict__ inv,
+                                                                 uint4 *__restrict__ xp, int k,
+                                                                 int HC) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 128 + threadIdx.x;
+  if (c >= HC) return;
+  int row[kMaxTopKPush];
+#pragma unroll
+  for (int j = 0; j < kMaxTopKPush; j++) row[j] = inv[t * k + min(j, k - 1)];
+  const uint4 v = x[(size_t)t * HC + c];
+#pragma unroll
+  for (int j = 0; j < kMaxTopKPush; j++)
+    if (j < k) xp[(size_t)row[j] * HC + c] = v;
+}
+
+void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T, int k,
+                               int H, hipStream_t s) {
+  const int HC = H / 8;
+  if (T <= 0) return;
+  hipLaunchKernelGGL(dispatch_push_bf16_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
+                     (const uint4 *)x, inv, (uint4 *)xp, k, HC);
+}
+
+// MX: each lane quantises 8 values as in dispatch_mx_kernel (a quad of lanes
+// per 32-value block), then stores codes, scale and round trip to k rows.
+__global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
+    const uint4 *__restrict__ x, const int32_t *__restrict__ inv, uint2 *__restrict__ xq,
+    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int T, int k, int HC /* H/8 */) {
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long)T * HC) return;
+  const int t = (int)(id / HC), c = (int)(id - (long)t * HC);
+  int row[kMaxTopKPush];
+#pragma unroll
+  for (int j = 0; j < kMaxTopKPush; j++) row[j] = inv[t * k + min(j, k - 1)];
+  float v[8];
+  unpack8(x[(size_t)t * HC + c], v);
+  uint2 codes;
+  float deq[8];
+  const uint32_t sc = mx_quad8(v, &codes, deq);
+  const uint4 hat = pack8(deq);
+#pragma unroll
+  for (int j = 0; j < kMaxTopKPush; j++) {
+    if (j < k) {
+      const size_t r = (size_t)row[j];
+      xq[r * HC + c] = codes;
+      if ((c & 3) == 0) xs[r * (HC / 4) + c / 4] = (uint8_t)sc;
+      if (xhat) xhat[r * HC + c] = hat;
+    }
+  }
+}
+
+void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq, uint8_t *xs,
+                             uint16_t *xhat, int T, int k, int H, hipStream_t s) {
+  const long n = (long)T * (H / 8);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(dispatch_push_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const uint4 *)x, inv, (uint2 *)xq, xs, (uint4 *)xhat, T, k, H / 8);
 }
 
 // Row-wise MX quantisation of a bf16 matrix along its contiguous axis.
