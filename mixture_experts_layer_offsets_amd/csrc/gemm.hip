@@ -282,16 +282,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
       oa[i] = (uint32_t)(row * (int)p.lda * 2 + c * 16);
       ob[i] = (uint32_t)(row * (int)p.ldb * 2 + c * 16);
     }
-    auto issue = [&](uint16_t *L, int kt) {
-      const int sa = kt * 64 * (int)p.lda * 2, sb = kt * 64 * (int)p.ldb * 2;
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
-                                                 oa[i], sa, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(L + 64 * BM + (wave * 8 + i) * 512),
-                                                 16, ob[i], sb, 0, 0);
+    const int nk = (Kg + 63) / 64;
+    // DMA instruction q (0-7: A rows, 8-15: B rows) of stage kt into L; a
+    // stage past the end selects an empty descriptor (zero fill, no traffic)
+    const __amdgpu_buffer_rsrc_t rNone =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, 0, kBufferDword3);
+    auto dma = [&](uint16_t *L, int kt, int q) {
+      const bool live = kt < nk;
+      if (q < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone,
+                                                 (lds_ptr_t)(L + (wave * 8 + q) * 512), 16, oa[q],
+                                                 live ? kt * 64 * (int)p.lda * 2 : 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            live ? rB : rNone, (lds_ptr_t)(L + 64 * BM + (wave * 8 + q - 8) * 512), 16,
+            ob[q - 8], live ? kt * 64 * (int)p.ldb * 2 : 0, 0, 0);
     };
     // fragment addresses: lane l in 16-lane group q = l / 16, j = l % 16
     const int q = lane >> 4, j = lane & 15;
@@ -309,7 +314,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
       __builtin_memcpy((char *)&f + 8, phi, 8);
       return f;
     };
-    auto compute = [&](const uint16_t *L) {
+    // One stage from L; the 16 DMA instructions of stage dkt into Ld go out
+    // one after every fourth MFMA (as a burst they stall the wave while the
+    // memory pipeline is backed up, and no MFMA issues meanwhile).
+    auto compute = [&](const uint16_t *L, uint16_t *Ld, int dkt) {
       const uint16_t *TA = L, *TB = L + 64 * BM;
       bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
@@ -329,32 +337,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++) {
 #pragma unroll
-          for (int jj = 0; jj < 4; jj++)
+          for (int jj = 0; jj < 4; jj++) {
             acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj],
                                                                  0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+            if (jj == 3) dma(Ld, dkt, 4 * ks + i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
     };
-    const int nk = (Kg + 63) / 64;
-    issue(L0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 16; q++) dma(L0, 0, q);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
-      issue(L1, kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(L0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      compute(L0, L1, kt + 1);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();
-      if (kt + 2 < nk) issue(L0, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(L1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      compute(L1, L0, kt + 2);  // zeros past the end
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();
     }
-    if (kt < nk) compute(L0);
+    if (kt < nk) compute(L0, L1, nk);  // zero fill, unused
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
   }
   epilogue<true, EPI>(p, acc, g, m0, n0, 0, p.M, wm0, wn0, lane);
 }

@@ -51,18 +51,22 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
   // sink a k-slice's MFMAs past the barrier.
   const __amdgpu_buffer_rsrc_t rNone =
       __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, 0, kBufferDword3);
-  auto issue = [&](uint16_t *L, int kt) {
+  // DMA instruction q (0-7: A rows, 8-15: B rows) of stage kt into L.
+  auto dma = [&](uint16_t *L, int kt, int q) {
     const bool live = kt < p.K / BK;
-    const __amdgpu_buffer_rsrc_t ra = live ? rA : rNone, rb = live ? rB : rNone;
     const int soff = live ? kt * BK * 2 : 0;
+    if (q < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone,
+                                               (lds_ptr_t)(L + (wave * 8 + q) * 512), 16, oa[q],
+                                               soff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          live ? rB : rNone, (lds_ptr_t)(L + BM * BK + (wave * 8 + q - 8) * 512), 16, ob[q - 8],
+          soff, 0, 0);
+  };
+  auto issue = [&](uint16_t *L, int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(L + (wave * 8 + i) * 512), 16,
-                                               oa[i], soff, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(L + BM * BK + (wave * 8 + i) * 512),
-                                               16, ob[i], soff, 0, 0);
+    for (int q = 0; q < 16; q++) dma(L, kt, q);
   };
   f32x16 acc[4][4];
 #pragma unroll
@@ -99,6 +103,9 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
   const int nk = p.K / BK;
   // Lc holds stage kt, Ln receives stage kt + 1 (in flight); Lc is refilled
   // with stage kt + 2 once every wave has its last fragments of stage kt.
+  // The refill's 16 DMA instructions are issued one after each of the last
+  // slice's 16 MFMAs: issued as one burst they stall the wave whenever the
+  // memory pipeline is backed up, and no MFMA issues meanwhile.
   auto stage = [&](uint16_t *Lc, const uint16_t *Ln, int kt) {
 #pragma unroll
     for (int ks = 0; ks < 3; ks++) {
@@ -109,11 +116,15 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    issue(Lc, kt + 2);  // zeros past the end
-    load(Ln, 0, 0);     // after the last stage this reads zeros, unused
+    load(Ln, 0, 0);  // after the last stage this reads zeros, unused
     __builtin_amdgcn_sched_barrier(0);
-    mma(1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          fa[1][q >> 2], fb[1][q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+      dma(Lc, kt + 2, q);  // zeros past the end
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   issue(L0, 0);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
@@ -194,18 +205,22 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   // MFMAs of a k-slice past the barrier and collapse the pipeline.
   const __amdgpu_buffer_rsrc_t rNone =
       __builtin_amdgcn_make_buffer_rsrc((void *)Ac, (short)0, 0, kBufferDword3);
-  auto issue = [&](uint8_t *L, int kt) {
+  // DMA instruction q (0-7: A rows, 8-15: B rows) of stage kt into L.
+  auto dma = [&](uint8_t *L, int kt, int q) {
     const bool live = kt < K / MXK;
-    const __amdgpu_buffer_rsrc_t ra = live ? rA : rNone, rb = live ? rB : rNone;
     const int soff = live ? kt * MXK : 0;
+    if (q < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone,
+                                               (lds_ptr_t)(L + (wave * 8 + q) * 1024), 16, oa[q],
+                                               soff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          live ? rB : rNone, (lds_ptr_t)(L + BM * MXK + (wave * 8 + q - 8) * 1024), 16,
+          ob[q - 8], soff, 0, 0);
+  };
+  auto issue = [&](uint8_t *L, int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(L + (wave * 8 + i) * 1024), 16,
-                                               oa[i], soff, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(L + BM * MXK + (wave * 8 + i) * 1024),
-                                               16, ob[i], soff, 0, 0);
+    for (int q = 0; q < 16; q++) dma(L, kt, q);
   };
   // scale dwords of this lane's rows: 4 blocks of 32 along K per stage
   const int fr = lane & 31, h = lane >> 5;
@@ -245,15 +260,16 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
                            (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
     }
   };
-  auto mma = [&](int ks, const int *sa, const int *sb) {
+  auto mma1 = [&](int ks, int i, int j, const int *sa, const int *sb) {
     const int sh = 8 * (2 * ks + h);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0, (sa[i] >> sh) & 0xFF, 0, (sb[j] >> sh) & 0xFF);
+  };
+  auto mma = [&](int ks, const int *sa, const int *sb) {
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0, (sa[i] >> sh) & 0xFF, 0,
-            (sb[j] >> sh) & 0xFF);
+      for (int j = 0; j < 4; j++) mma1(ks, i, j, sa, sb);
   };
 
   const int nk = K / MXK;
@@ -266,11 +282,15 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    issue(Lc, kt + 2);  // zeros past the end
-    load(Ln, 0, 0);     // after the last stage this reads zeros, unused
+    load(Ln, 0, 0);  // after the last stage this reads zeros, unused
     __builtin_amdgcn_sched_barrier(0);
-    mma(1, sa, sb);
-    __builtin_amdgcn_sched_barrier(0);
+    // the refill's DMA instructions one after each MFMA (see nt_tile)
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      mma1(1, q >> 2, q & 3, sa, sb);
+      dma(Lc, kt + 2, q);  // zeros past the end
+      __builtin_amdgcn_sched_barrier(0);
+    }
     load_scales(min(kt + 2, nk - 1), sa, sb);
   };
   issue(L0, 0);
