@@ -103,12 +103,25 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
   const int nk = p.K / BK;
   // Lc holds stage kt, Ln receives stage kt + 1 (in flight); Lc is refilled
   // with stage kt + 2 once every wave has its last fragments of stage kt.
-  // The refill's 16 DMA instructions are issued one after each of the last
-  // slice's 16 MFMAs: issued as one burst they stall the wave whenever the
-  // memory pipeline is backed up, and no MFMA issues meanwhile.
-  auto stage = [&](uint16_t *Lc, const uint16_t *Ln, int kt) {
+  // The refill's 16 DMA instructions are spread over 32 MFMAs: 0-7 after
+  // every second MFMA of the last k-slice, 8-15 after every second MFMA of
+  // the next stage's first slice.  Issued as one burst they stall the wave
+  // whenever the memory pipeline is backed up, and no MFMA issues meanwhile.
+  auto mma_dma = [&](int set, uint16_t *Ld, int dkt, int d0) {
 #pragma unroll
-    for (int ks = 0; ks < 3; ks++) {
+    for (int q = 0; q < 16; q++) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          fa[set][q >> 2], fb[set][q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+      if (q & 1) dma(Ld, dkt, d0 + (q >> 1));  // zeros past the end
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt) {
+    load(Lc, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+#pragma unroll
+    for (int ks = 1; ks < 3; ks++) {
       load(Lc, ks + 1, (ks + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       mma(ks & 1);
@@ -118,18 +131,13 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
     __syncthreads();
     load(Ln, 0, 0);  // after the last stage this reads zeros, unused
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          fa[1][q >> 2], fb[1][q & 3], acc[q >> 2][q & 3], 0, 0, 0);
-      dma(Lc, kt + 2, q);  // zeros past the end
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    mma_dma(1, Lc, kt + 2, 0);  // first half of Lc's refill
   };
   issue(L0, 0);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  issue(L1, 1);
+#pragma unroll
+  for (int q = 0; q < 8; q++) dma(L1, 1, q);
   load(L0, 0, 0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
