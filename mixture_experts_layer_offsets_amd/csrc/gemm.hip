@@ -314,55 +314,67 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
       __builtin_memcpy((char *)&f + 8, phi, 8);
       return f;
     };
-    // One stage from L; the 16 DMA instructions of stage dkt into Ld go out
-    // one after every fourth MFMA (as a burst they stall the wave while the
-    // memory pipeline is backed up, and no MFMA issues meanwhile).
-    auto compute = [&](const uint16_t *L, uint16_t *Ld, int dkt) {
-      const uint16_t *TA = L, *TB = L + 64 * BM;
-      bf16x8 fa[2][4], fb[2][4];
+    // The row-ragged tile's pipeline (row_tile.h): fragments double buffered
+    // across the whole K loop; the wait and the barrier after the third
+    // k-slice; the refill of the buffer just finished (stage kt + 2) spread
+    // over 32 MFMAs, DMAs 0-7 after every second MFMA of the last slice and
+    // 8-15 after every second MFMA of the next stage's first slice.
+    bf16x8 fa[2][4], fb[2][4];
+    auto load = [&](const uint16_t *L, int ks, int set) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        fa[0][i] = frag(TA, krow, colA + 32 * i);
-        fb[0][i] = frag(TB, krow, colB + 32 * i);
+        fa[set][i] = frag(L, 16 * ks + krow, colA + 32 * i);
+        fb[set][i] = frag(L + 64 * BM, 16 * ks + krow, colB + 32 * i);
       }
+    };
+    auto mma = [&](int set) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        const int c = ks & 1, nx = c ^ 1;
-        if (ks + 1 < 4) {
+      for (int i = 0; i < 4; i++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            fa[nx][i] = frag(TA, 16 * (ks + 1) + krow, colA + 32 * i);
-            fb[nx][i] = frag(TB, 16 * (ks + 1) + krow, colB + 32 * i);
-          }
-        }
+        for (int jj = 0; jj < 4; jj++)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][jj],
+                                                               acc[i][jj], 0, 0, 0);
+    };
+    auto mma_dma = [&](int set, uint16_t *Ld, int dkt, int d0) {
+#pragma unroll
+      for (int q = 0; q < 16; q++) {
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fa[set][q >> 2], fb[set][q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+        if (q & 1) dma(Ld, dkt, d0 + (q >> 1));  // zeros past the end
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj],
-                                                                 0, 0, 0);
-            if (jj == 3) dma(Ld, dkt, 4 * ks + i);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
       }
+    };
+    auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt) {
+      load(Lc, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+#pragma unroll
+      for (int ks = 1; ks < 3; ks++) {
+        load(Lc, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+      load(Ln, 0, 0);  // after the last stage this reads zeros, unused
+      __builtin_amdgcn_sched_barrier(0);
+      mma_dma(1, Lc, kt + 2, 0);  // first half of Lc's refill
     };
 #pragma unroll
     for (int q = 0; q < 16; q++) dma(L0, 0, q);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; q++) dma(L1, 1, q);
+    load(L0, 0, 0);
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      compute(L0, L1, kt + 1);
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();
-      compute(L1, L0, kt + 2);  // zeros past the end
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();
+    for (; kt + 2 <= nk; kt += 2) {
+      stage(L0, L1, kt);
+      stage(L1, L0, kt + 1);
     }
-    if (kt < nk) compute(L0, L1, nk);  // zero fill, unused
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if (kt < nk) stage(L0, L1, kt);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
   }
   epilogue<true, EPI>(p, acc, g, m0, n0, 0, p.M, wm0, wn0, lane);
 }
