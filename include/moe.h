@@ -166,8 +166,13 @@ int moe_layout(const moe_shape *shape, const int32_t *topk_idx,
 /* Dispatch (gather-permute): row r of x_perm is a copy of token
  * perm[r] / k of x -- the destination-driven read the pages call pull
  * dispatch [KC §02].  bf16: x_perm is uint16_t [R][H], x_scale unused.
- * MXFP8: x_perm is E4M3 codes uint8 [R][H] and x_scale E8M0 uint8
- * [R][H/32], quantised along H as the row is copied [KC §02]. */
+ * MXFP8: x_perm is E4M3 codes uint8 [R][H] and x_scale the E8M0 scales,
+ * one per 32 values along H, quantised as the row is copied [KC §02].
+ * MX scale layout (x_scale here and every E8M0 array below): K-blocked,
+ * [K/128][rows][4] -- the scale of row r and 32-block b of a [rows][K]
+ * matrix is byte (b/4 * rows + r) * 4 + b%4, so the scales of one 128-wide
+ * K slice of consecutive rows are consecutive dwords (what a GEMM tile
+ * reads per stage).  rows = R here. */
 int moe_dispatch(const moe_shape *shape, const uint16_t *x,
                  const int32_t *perm, void *x_perm, uint8_t *x_scale,
                  void *stream);
@@ -240,12 +245,12 @@ typedef struct moe_saved_view {
   int32_t *perm;      /* [R] */
   int32_t *inv_perm;  /* [R] */
   void *x_perm;       /* bf16 [R][H] (bf16), or E4M3 codes [R][H] (MXFP8) */
-  uint8_t *x_scale;   /* E8M0 [R][H/32] (MXFP8) */
+  uint8_t *x_scale;   /* E8M0, K-blocked [H/128][R][4] (MXFP8) */
   uint16_t *x_hat;    /* bf16 [R][H]: MX round trip of the dispatched rows (MXFP8) */
   uint16_t *gu;       /* bf16 [R][2I]: g and u, interleaved in 32-column blocks */
   uint16_t *act;      /* bf16 [R][I]: a (bf16) or its MX round trip (MXFP8) */
   uint8_t *act_q;     /* E4M3 [R][I] (MXFP8) */
-  uint8_t *act_scale; /* E8M0 [R][I/32] (MXFP8) */
+  uint8_t *act_scale; /* E8M0, K-blocked [I/128][R][4] (MXFP8) */
   uint16_t *y;        /* bf16 [R][H] */
   uint16_t *y_shared; /* bf16 [T][H] (shared expert) */
 } moe_saved_view;

@@ -291,7 +291,7 @@ void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_
     launch_gemm_rows(p, EPI_SWIGLU, true, (int)max_rows, s);
   } else {
     p.A = (const uint16_t *)xq.q; p.B = (const uint16_t *)W.guTq.q;
-    const MxOperands m{xq.s, W.guTq.s, 2 * I * (H / 32), aq.q, aq.s};
+    const MxOperands m{xq.s, W.guTq.s, (int)max_rows, aq.q, aq.s};
     launch_gemm_rows_mx(p, m, EPI_SWIGLU, (int)max_rows, s);
   }
   if (st) st->mark(mark);
@@ -305,7 +305,7 @@ void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_
     launch_gemm_rows(q, EPI_BF16, true, (int)max_rows, s);
   } else {
     q.A = (const uint16_t *)aq.q; q.B = (const uint16_t *)W.dTq.q;
-    const MxOperands m{aq.s, W.dTq.s, H * (I / 32), nullptr, nullptr};
+    const MxOperands m{aq.s, W.dTq.s, (int)max_rows, nullptr, nullptr};
     launch_gemm_rows_mx(q, m, EPI_BF16, (int)max_rows, s);
   }
   if (st) st->mark(mark + 1);
@@ -333,7 +333,7 @@ void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
   } else {
     launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
     a.A = (const uint16_t *)dyq.q; a.B = (const uint16_t *)W.dq.q;
-    const MxOperands m{dyq.s, W.dq.s, I * (H / 32), nullptr, nullptr};
+    const MxOperands m{dyq.s, W.dq.s, (int)max_rows, nullptr, nullptr};
     launch_gemm_rows_mx(a, m, EPI_SWIGLU_BWD, (int)max_rows, s);
   }
   if (st) st->mark(mark);
@@ -356,7 +356,7 @@ void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
   } else {
     launch_quant_rows_mx(dh, (int)max_rows, (int)(2 * I), dhq.q, dhq.s, s);
     c.A = (const uint16_t *)dhq.q; c.B = (const uint16_t *)W.guq.q;
-    const MxOperands m{dhq.s, W.guq.s, H * (2 * I / 32), nullptr, nullptr};
+    const MxOperands m{dhq.s, W.guq.s, (int)max_rows, nullptr, nullptr};
     launch_gemm_rows_mx(c, m, EPI_BF16, (int)max_rows, s);
   }
   if (st) st->mark(mark + 2);
@@ -417,9 +417,9 @@ int mk_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Save
     a.g2.A = sv.act; a.g2.B = p.r.dT;
   } else {
     a.g1.A = (const uint16_t *)sv.xq.q; a.g1.B = (const uint16_t *)p.r.guTq.q;
-    a.mx1 = MxOperands{sv.xq.s, p.r.guTq.s, 2 * I * (H / 32), sv.aq.q, sv.aq.s};
+    a.mx1 = MxOperands{sv.xq.s, p.r.guTq.s, (int)d.R, sv.aq.q, sv.aq.s};
     a.g2.A = (const uint16_t *)sv.aq.q; a.g2.B = (const uint16_t *)p.r.dTq.q;
-    a.mx2 = MxOperands{sv.aq.s, p.r.dTq.s, H * (I / 32), nullptr, nullptr};
+    a.mx2 = MxOperands{sv.aq.s, p.r.dTq.s, (int)d.R, nullptr, nullptr};
   }
   if (d.shared) {
     a.sg1.C = sv.act_s; a.sg1.ldc = Is; a.sg1.C2 = sv.gu_s; a.sg1.ldc2 = 2 * Is;
@@ -433,9 +433,9 @@ int mk_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Save
     } else {
       launch_dispatch_mx(x, nullptr, sv.xq_s.q, sv.xq_s.s, sv.xhat_s, (int)d.T, 1, (int)H, s);
       a.sg1.A = (const uint16_t *)sv.xq_s.q; a.sg1.B = (const uint16_t *)p.s.guTq.q;
-      a.smx1 = MxOperands{sv.xq_s.s, p.s.guTq.s, 2 * Is * (H / 32), sv.aq_s.q, sv.aq_s.s};
+      a.smx1 = MxOperands{sv.xq_s.s, p.s.guTq.s, (int)d.T, sv.aq_s.q, sv.aq_s.s};
       a.sg2.A = (const uint16_t *)sv.aq_s.q; a.sg2.B = (const uint16_t *)p.s.dTq.q;
-      a.smx2 = MxOperands{sv.aq_s.s, p.s.dTq.s, H * (Is / 32), nullptr, nullptr};
+      a.smx2 = MxOperands{sv.aq_s.s, p.s.dTq.s, (int)d.T, nullptr, nullptr};
     }
   }
   a.y = sv.y; a.ys = sv.y_s; a.out = out;

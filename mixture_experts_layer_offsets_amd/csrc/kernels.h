@@ -86,12 +86,17 @@ void launch_gemm_rows(const GemmArgs &p, int epi, bool b_kcontig, int max_rows, 
 // with scales [G][N][K/32].  Epilogues: EPI_BF16, EPI_SWIGLU (with
 // p.mx_out: a quantised along I into codes/scales, and its bf16 round trip
 // into p.C), EPI_SWIGLU_BWD.
+//
+// E8M0 scales are stored K-blocked: for a matrix of `rows` rows, the scale of
+// row r and 32-wide block b is byte (b/4 * rows + r) * 4 + b%4, i.e.
+// [K/128][rows][4].  A GEMM stage (128 values of K) then finds the scales of
+// a tile's consecutive rows in consecutive dwords.
 struct MxOperands {
-  const uint8_t *a_scale;   // [rows][K/32]
-  const uint8_t *b_scale;   // [G][N][K/32]
-  long sBs;                 // per-group stride of b_scale (bytes)
+  const uint8_t *a_scale;   // A scales, [K/128][a_rows][4]
+  const uint8_t *b_scale;   // B scales, [K/128][G*N][4] (row g*N + n)
+  int a_rows;               // rows of the A scale matrix
   uint8_t *q_out;           // SwiGLU MX epilogue: a codes [rows][I]
-  uint8_t *s_out;           // SwiGLU MX epilogue: a scales [rows][I/32]
+  uint8_t *s_out;           // SwiGLU MX epilogue: a scales, [I/128][a_rows][4]
 };
 void launch_gemm_rows_mx(const GemmArgs &p, const MxOperands &mx, int epi, int max_rows,
                          hipStream_t s);

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(
   float deq[8];
   const uint32_t sc = mx_quad8(v, &codes, deq);
   xq[(size_t)r * HC + c] = codes;
-  if ((c & 3) == 0) xs[(size_t)r * (HC / 4) + c / 4] = (uint8_t)sc;
+  // scales K-blocked: block b = c/4 of row r at byte (b/4 * R + r) * 4 + b%4
+  if ((c & 3) == 0) xs[((size_t)(c >> 4) * R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
   if (xhat) xhat[(size_t)r * HC + c] = pack8(deq);
 }
 
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
     uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int T, int k, int HC /* H/8 */) {
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
   if (id >= (long)T * HC) return;
+  const long R = (long)T * k;  // rows of the output (scale plane stride)
   const int t = (int)(id / HC), c = (int)(id - (long)t * HC);
   int row[kMaxTopKPush];
 #pragma unroll
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
     if (j < k) {
       const size_t r = (size_t)row[j];
       xq[r * HC + c] = codes;
-      if ((c & 3) == 0) xs[r * (HC / 4) + c / 4] = (uint8_t)sc;
+      if ((c & 3) == 0) xs[((size_t)(c >> 4) * R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
       if (xhat) xhat[r * HC + c] = hat;
     }
   }

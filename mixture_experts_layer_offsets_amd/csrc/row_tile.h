@@ -193,11 +193,14 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(Bc + (size_t)g * p.sB + (size_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb,
       kBufferDword3);
+  // K-blocked scales: stage kt's dword for A row r at (kt * a_rows + r) * 4,
+  // for B row n of group g at (kt * G*N + g*N + n) * 4
+  const int b_rows_all = p.G * p.N;
   const __amdgpu_buffer_rsrc_t rSa = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(mx.a_scale + (size_t)(rowbase + m0) * KS), (short)0, a_rows * KS, kBufferDword3);
+      (void *)mx.a_scale, (short)0, mx.a_rows * KS, kBufferDword3);
   const __amdgpu_buffer_rsrc_t rSb = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(mx.b_scale + (size_t)g * mx.sBs + (size_t)n0 * KS), (short)0, b_rows * KS,
-      kBufferDword3);
+      (void *)mx.b_scale, (short)0, b_rows_all * KS, kBufferDword3);
+  const int sa_row = rowbase + m0 + wm0, sb_row = g * p.N + n0 + wn0;
 
   uint32_t oa[8], ob[8];
 #pragma unroll
@@ -230,13 +233,16 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
 #pragma unroll
     for (int q = 0; q < 16; q++) dma(L, kt, q);
   };
-  // scale dwords of this lane's rows: 4 blocks of 32 along K per stage
+  // scale dwords of this lane's rows (4 blocks of 32 along K per stage); 32
+  // consecutive rows' dwords are one 128-byte line
   const int fr = lane & 31, h = lane >> 5;
   auto load_scales = [&](int kt, int *sa, int *sb) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      sa[i] = __builtin_amdgcn_raw_buffer_load_b32(rSa, (wm0 + 32 * i + fr) * KS + kt * 4, 0, 0);
-      sb[i] = __builtin_amdgcn_raw_buffer_load_b32(rSb, (wn0 + 32 * i + fr) * KS + kt * 4, 0, 0);
+      sa[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rSa, (kt * mx.a_rows + sa_row + 32 * i + fr) * 4, 0, 0);
+      sb[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rSb, (kt * b_rows_all + sb_row + 32 * i + fr) * 4, 0, 0);
     }
   };
 

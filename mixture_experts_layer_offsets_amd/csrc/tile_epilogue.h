@@ -168,7 +168,8 @@ __device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOpera
       uint4 *dh = (uint4 *)((uint16_t *)p.C + grow * p.ldc + a0 + blk * 32);
 #pragma unroll
       for (int c = 0; c < 4; c++) dh[c] = pack8(deq + 8 * c);
-      mx->s_out[grow * (I / 32) + a0 / 32 + blk] = (uint8_t)sc;
+      const int b = a0 / 32 + blk;  // 32-block of a along I; scales K-blocked
+      mx->s_out[((size_t)(b >> 2) * mx->a_rows + grow) * 4 + (b & 3)] = (uint8_t)sc;
     }
   }
 }

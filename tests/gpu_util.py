@@ -48,6 +48,14 @@ def check_rel(name, gpu, ref, tol):
     return e
 
 
+def unblock_scales(s, rows, K):
+    """E8M0 scales as the library stores them, K-blocked ([K/128][rows][4]:
+    the scale of row r, block b at (b/4 * rows + r) * 4 + b%4), to the
+    oracle's [rows][K/32]."""
+    a = np.asarray(s).reshape(K // 128, rows, 4)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(rows, K // 32))
+
+
 def note(msg: str):
     """Print and flush a progress line (names the case before GPU work)."""
     print(msg, flush=True)

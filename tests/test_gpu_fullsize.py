@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL_BF16, TOL_MX, Run, bf, check_rel, host, note
+from gpu_util import TOL_BF16, TOL_MX, Run, bf, check_rel, host, note, unblock_scales
 from oracle.layer import TokenEvaluator, expert_weight_grad_columns
 from oracle.numerics import bf16_bits, bf16_to_f64
 
@@ -42,10 +42,10 @@ def _check_dispatch_mx(run, perm, k, H, rng, n_rows=512):
     codes, scales = oracle.dispatch(run.inp["x"], perm[rows], k, mx=True)
     rt = torch.as_tensor(rows, device="cuda")
     xq = run.saved("x_perm", torch.uint8, (R, H)).index_select(0, rt)
-    xs = run.saved("x_scale", torch.uint8, (R, H // 32)).index_select(0, rt)
+    xs = unblock_scales(host(run.saved("x_scale", torch.uint8, (R, H // 32))), R, H)[rows]
     xh = run.saved("x_hat", torch.int16, (R, H)).index_select(0, rt)
     assert np.array_equal(host(xq), codes)
-    assert np.array_equal(host(xs), scales)
+    assert np.array_equal(xs, scales)
     ref_hat = oracle.mx.mx_dequantize(codes, scales, axis=1)
     assert np.array_equal(host(xh).view(np.uint16), bf16_bits(ref_hat))
 

@@ -17,7 +17,7 @@ import torch
 import mixture_experts_layer_offsets_amd as m
 import oracle
 import synth
-from gpu_util import TOL_MX, Run, bf, check_rel, dev, host, note
+from gpu_util import TOL_MX, Run, bf, check_rel, dev, host, note, unblock_scales
 from oracle.mx import e4m3_decode, e4m3_encode, mx_dequantize
 from oracle.numerics import bf16_bits
 
@@ -89,7 +89,7 @@ def test_dispatch_mx_bit_exact(T, H, k):
     m.moe_dispatch(shape, dev(x), dev(perm), xq, xs)
     torch.cuda.synchronize()
     codes, scales = oracle.dispatch(x, perm, k, mx=True)
-    _assert_codes_equal("scales", host(xs), scales)
+    _assert_codes_equal("scales", unblock_scales(host(xs), R, H), scales)
     _assert_codes_equal("codes", host(xq), codes)
 
 
@@ -198,12 +198,13 @@ def check_layer_mx(run, fw, bw, tol=TOL_MX):
     # dispatch: codes, scales and round trip of the rows the GPU laid out
     codes, scales = oracle.dispatch(run.inp["x"], perm, k, mx=True)
     assert np.array_equal(host(run.saved("x_perm", torch.uint8, (R, H))), codes)
-    assert np.array_equal(host(run.saved("x_scale", torch.uint8, (R, H // 32))), scales)
+    xs = unblock_scales(host(run.saved("x_scale", torch.uint8, (R, H // 32))), R, H)
+    assert np.array_equal(xs, scales)
     xh = host(run.saved("x_hat", torch.int16, (R, H))).view(np.uint16)
     assert np.array_equal(xh, bf16_bits(mx_dequantize(codes, scales, axis=1)))
     # the activation's codes and its bf16 round trip agree with each other
     aq = host(run.saved("act_q", torch.uint8, (R, I)))
-    as_ = host(run.saved("act_scale", torch.uint8, (R, I // 32)))
+    as_ = unblock_scales(host(run.saved("act_scale", torch.uint8, (R, I // 32))), R, I)
     act = bf(run.saved("act", torch.int16, (R, I)))
     assert np.array_equal(act, mx_dequantize(aq, as_, axis=1))
     if not amb.any():
