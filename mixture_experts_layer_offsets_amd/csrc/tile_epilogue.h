@@ -44,15 +44,35 @@ __device__ __forceinline__ void copy_rows_out(const uint8_t *plane, int nch, int
 }
 
 // Copy rows from global memory (src, pitch ld bytes) into a plane; rows past
-// rows_valid or chunks past col_bytes are left unwritten.
+// rows_valid or chunks past col_bytes are left unwritten (rows_valid >= 1,
+// col_bytes >= 16).  Each thread issues a batch of loads before its first LDS
+// store, so the copy costs a few memory round trips rather than one per
+// chunk; loads of skipped chunks read a valid chunk instead and are dropped.
+constexpr int kRowsInBatch = 16;
+
 __device__ __forceinline__ void copy_rows_in(uint8_t *plane, int nch, int rows, int rows_valid,
                                              int col_bytes, const uint8_t *src, long ld,
                                              int tid) {
   const int n = rows * nch;
-  for (int idx = tid; idx < n; idx += NT) {
-    const int r = idx / nch, ch = idx - (idx / nch) * nch;
-    if (r < rows_valid && ch * 16 < col_bytes)
-      *(uint4 *)(plane + st_off(r, ch, nch)) = *(const uint4 *)(src + (size_t)r * ld + ch * 16);
+  const int last_ch = (col_bytes - 1) >> 4;
+  for (int i0 = tid; i0 < n; i0 += NT * kRowsInBatch) {
+    uint4 v[kRowsInBatch];
+#pragma unroll
+    for (int u = 0; u < kRowsInBatch; u++) {
+      const int idx = min(i0 + NT * u, n - 1);
+      const int r = idx / nch, ch = idx - (idx / nch) * nch;
+      v[u] = *(const uint4 *)(src + (size_t)min(r, rows_valid - 1) * ld + min(ch, last_ch) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsInBatch; u++)
+      asm volatile("" ::"v"(v[u].x), "v"(v[u].y), "v"(v[u].z), "v"(v[u].w));
+#pragma unroll
+    for (int u = 0; u < kRowsInBatch; u++) {
+      const int idx = i0 + NT * u;
+      const int r = idx / nch, ch = idx - (idx / nch) * nch;
+      if (idx < n && r < rows_valid && ch * 16 < col_bytes)
+        *(uint4 *)(plane + st_off(r, ch, nch)) = v[u];
+    }
   }
 }
 
