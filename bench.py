@@ -53,6 +53,12 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the bounded oracle sample (CPU baseline)")
+    ap.add_argument("--schedule", choices=("staged", "pipelined"), default="staged",
+                    help="schedule whose throughput is `value` (both are timed and reported)")
+    ap.add_argument("--minibatch-rows", type=int, default=0,
+                    help="pipelined schedule: routed rows per minibatch (0 = library default)")
+    ap.add_argument("--comm-cus", type=int, default=0,
+                    help="pipelined schedule: CUs of the communication stream (0 = share all)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -206,17 +212,55 @@ def main():
         if w.backward:
             layer.backward(dout, x, w_router=wr, grads=grads, sched=sb)
 
+    def pipelined():
+        s = m.MoeSched()
+        s.schedule = m.MOE_SCHED_PIPELINED
+        s.minibatch_rows = a.minibatch_rows
+        s.comm_cus = a.comm_cus
+        return s
+
+    def timed_loop(sf=None, sb=None):
+        """K steps of one schedule, no stage events: seconds of wall clock."""
+        for _ in range(a.warmup):
+            step(sf, sb)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            step(sf, sb)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    # the timed steps of each schedule
+    sp = pipelined()
+    wall = {"staged": timed_loop(), "pipelined": timed_loop(sp, sp)}
+    elapsed = wall[a.schedule]
+    ms = elapsed / a.steps * 1e3
+
+    # per-stage times (staged schedule, HIP events on the layer's stream)
     for _ in range(a.warmup):
         step()
     ev = [(make_events(n_f), make_events(n_b)) for _ in range(a.steps)]
     scheds = [(sched_for(f), sched_for(b)) for f, b in ev]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for (sf, _), (sb, _) in scheds:
         step(sf, sb)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed / a.steps * 1e3
+    # forward / backward split of the pipelined schedule (events at its joins)
+    pev = [(make_events(n_f), make_events(n_b)) for _ in range(a.steps)]
+    psched = []
+    for f, b in pev:
+        (pf, af), (pb, ab) = sched_for(f), sched_for(b)
+        for q in (pf, pb):
+            q.schedule = m.MOE_SCHED_PIPELINED
+            q.minibatch_rows = a.minibatch_rows
+            q.comm_cus = a.comm_cus
+        psched.append(((pf, af), (pb, ab)))
+    torch.cuda.synchronize()
+    for (pf, _), (pb, _) in psched:
+        step(pf, pb)
+    torch.cuda.synchronize()
+    pipe_fwd = float(np.mean([f[0].elapsed_time(f[-1]) for f, _ in pev]))
+    pipe_bwd = float(np.mean([b[0].elapsed_time(b[-1]) for _, b in pev])) if w.backward else None
 
     stage_ms = {}
     for i, name in enumerate(FWD_STAGES):
@@ -269,6 +313,11 @@ def main():
         "hbm_frac": hbm,
         "layer_fwd_ms": sum(stage_ms[n] for n in FWD_STAGES),
         "layer_bwd_ms": sum(stage_ms[n] for n in BWD_STAGES) if w.backward else None,
+        "schedule": a.schedule,
+        "schedules_ms_per_step": {k: v / a.steps * 1e3 for k, v in wall.items()},
+        "pipelined": {"layer_fwd_ms": pipe_fwd, "layer_bwd_ms": pipe_bwd,
+                      "minibatch_rows": a.minibatch_rows or "default",
+                      "comm_cus": a.comm_cus},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, min(a.cpu_tokens, w.T))

@@ -76,6 +76,30 @@ typedef struct moe_shape {
   int32_t dtype;        /* MOE_BF16 or MOE_MXFP8 */
 } moe_shape;
 
+/* How the layer's forward and backward are scheduled (moe_sched.schedule).
+ *
+ * MOE_SCHED_STAGED: one kernel per step over all rows, on the caller's
+ *   stream.
+ * MOE_SCHED_PERSISTENT: the forward as one persistent kernel with a CU split
+ *   and device flags.  Switched off: refused with MOE_ERR_UNSUPPORTED.
+ * MOE_SCHED_PIPELINED: the rows go through the experts in minibatches
+ *   [KC §02]: minibatch m's dispatch overlaps the GEMMs of earlier
+ *   minibatches, and each token is combined as soon as the minibatch holding
+ *   its last routed row is done.  Dispatch, combine and their backward
+ *   mirrors run on a communication stream; the GEMMs of even and odd
+ *   minibatches run on two GEMM streams, so one minibatch's GEMMs can fill the
+ *   compute units the previous one leaves idle.  All ordering is by HIP events
+ *   on the GPU, with no host wait per minibatch [KC §02].  The backward walks
+ *   the minibatches in reverse [NA design].  With comm_cus > 0 the
+ *   communication stream is limited to comm_cus CUs and the GEMM streams to
+ *   the rest (hardware CU masks); with comm_cus = 0 all three share every CU.
+ *   The streams and events are the library's own, created on the first
+ *   pipelined call on each device and kept until the process ends; pipelined
+ *   calls on one device are enqueued one at a time (a mutex) and run on the
+ *   same streams, so they execute in call order.  Outputs are bit-identical
+ *   to MOE_SCHED_STAGED. */
+enum { MOE_SCHED_STAGED = 0, MOE_SCHED_PERSISTENT = 1, MOE_SCHED_PIPELINED = 2 };
+
 /* Schedule knobs of the layer call.  The pages retune the minibatch and the
  * number of communication processors per model shape [KC §03]; 0 always
  * means "library default".
@@ -85,26 +109,25 @@ typedef struct moe_shape {
  * boundary i, for i < n_stage_events, so a caller can time each stage:
  *   forward : 0 start, 1 routing+layout done, 2 dispatch done, 3 gate/up
  *             GEMM + SwiGLU done, 4 down GEMM done, 5 shared expert done,
- *             6 combine done (with use_megakernel, 2-5 are recorded when
- *             the persistent kernel, which runs dispatch, both GEMMs, the
- *             shared expert and combine together, has finished);
+ *             6 combine done (pipelined: 2-6 are recorded when all streams
+ *             have joined the caller's stream again);
  *   backward: 0 start, 1 reverse-combine done, 2 down data-gradient GEMM
  *             (+ SwiGLU backward) done, 3 down weight-gradient GEMM done,
  *             4 gate/up data-gradient GEMM done, 5 gate/up weight-gradient
  *             GEMM done, 6 shared expert done, 7 router + reverse-dispatch
- *             done. */
+ *             done (pipelined: 1-7 at the join). */
 typedef struct moe_sched {
-  int32_t minibatch_rows; /* routed rows per minibatch (0 = default) */
-  int32_t ring_slots;     /* slots of the on-device ring (0 = default) */
-  int32_t comm_cus;       /* CUs given to dispatch/combine (0 = default) */
-  int32_t use_megakernel; /* 0 = staged kernels, 1 = persistent pipelined
-                             kernel (currently refused with
-                             MOE_ERR_UNSUPPORTED: switched off) */
+  int32_t minibatch_rows; /* routed rows per minibatch (0 = default: enough
+                             rows for two full waves of gate/up GEMM tiles;
+                             at least max(256, ceil(R / 1024))) */
+  int32_t ring_slots;     /* minibatches dispatched ahead of the gate/up GEMM
+                             (0 = default, 2) */
+  int32_t comm_cus;       /* CUs given to dispatch/combine (0 = share all) */
+  int32_t schedule;       /* MOE_SCHED_* (0 = staged) */
   void **stage_events;    /* hipEvent_t[n_stage_events] or NULL */
   int32_t n_stage_events;
-  int32_t watchdog_us;    /* persistent kernel: microseconds one wait may take
-                             before it gives up and the layer reports
-                             MOE_ERR_DEVICE_TIMEOUT (0 = default, 2 s) */
+  int32_t watchdog_us;    /* persistent kernel only: microseconds one wait may
+                             take before it gives up (0 = default, 2 s) */
 } moe_sched;
 
 /* ------------------------------------------------------------------ sizes */

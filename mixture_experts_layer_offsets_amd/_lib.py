@@ -22,6 +22,9 @@ MOE_ERR_HIP = 4
 MOE_ERR_DEVICE_TIMEOUT = 5
 MOE_BF16 = 0
 MOE_MXFP8 = 1
+MOE_SCHED_STAGED = 0
+MOE_SCHED_PERSISTENT = 1
+MOE_SCHED_PIPELINED = 2
 
 c_void_p = ctypes.c_void_p
 c_size_t = ctypes.c_size_t
@@ -37,7 +40,7 @@ class MoeShape(ctypes.Structure):
 
 class MoeSched(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
-                ("comm_cus", ctypes.c_int32), ("use_megakernel", ctypes.c_int32),
+                ("comm_cus", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(c_void_p)), ("n_stage_events", ctypes.c_int32),
                 ("watchdog_us", ctypes.c_int32)]
 

@@ -13,6 +13,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -27,7 +29,7 @@ constexpr size_t kAlign = 256;
 
 // The persistent forward (megakernel.hip) stays off until the reason its
 // first GPU runs never finished is found; moe_layer_fwd then refuses
-// use_megakernel with MOE_ERR_UNSUPPORTED.
+// MOE_SCHED_PERSISTENT with MOE_ERR_UNSUPPORTED.
 constexpr bool kMegakernelEnabled = false;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -143,6 +145,9 @@ struct Work {
   // persistent forward: plan and counters (sized for the smallest minibatch)
   int32_t *mt_list, *mt_off, *ph, *cph, *tl, *tl_off, *tok_m, *counters;
   int max_nm, max_tiles, n_counters;
+  // pipelined schedule: per-minibatch group offsets and tile prefixes, and
+  // the token lists of the forward combine and the backward reverse-dispatch
+  int32_t *pm_off, *pm_ts, *tlf, *tlf_off, *tlb, *tlb_off;
 };
 
 // Smallest minibatch the persistent forward accepts, and its count bound.
@@ -172,6 +177,12 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   t.tok_m = c.take<int32_t>(d.T);
   t.n_counters = 2 + 3 * t.max_nm + t.max_tiles + (int)((d.T + 255) / 256) + 1;
   t.counters = c.take<int32_t>(t.n_counters);
+  t.pm_off = c.take<int32_t>((long)t.max_nm * (d.E + 1));
+  t.pm_ts = c.take<int32_t>((long)t.max_nm * (d.E + 1));
+  t.tlf = c.take<int32_t>(d.T);
+  t.tlf_off = c.take<int32_t>(t.max_nm + 1);
+  t.tlb = c.take<int32_t>(d.T);
+  t.tlb_off = c.take<int32_t>(t.max_nm + 1);
   const size_t union_start = c.off;
   // forward-only pieces (standalone expert FFN)
   t.act = c.take<uint16_t>(d.R * d.I);
@@ -275,11 +286,12 @@ void pack_wset(const WSet &w, int G, int H, int I, const uint16_t *wg, const uin
 // Expert FFN over row-ragged groups: a = silu(X Wg) * (X Wu); y = a Wd.
 // bf16: rows x.  MXFP8: rows xq (codes + scales); a is quantised in the
 // gate/up epilogue (codes and scales into aq, round trip into act) and the
-// down GEMM consumes the codes.
-void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_t *tiles, int G,
-                 long max_rows, long H, long I, const WSet &W, bool mx, uint16_t *act,
-                 uint16_t *gu, MxT aq, uint16_t *y, hipStream_t s, const Stages *st = nullptr,
-                 int mark = 0) {
+// down GEMM consumes the codes.  `grid_rows` bounds the rows the groups cover
+// (it sizes the grid); `a_rows` is the row count of the MX scale planes (the
+// whole row set, also when the groups cover only a minibatch of it).
+void gemm_gate_up(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_t *tiles, int G,
+                  long grid_rows, long a_rows, long H, long I, const WSet &W, bool mx,
+                  uint16_t *act, uint16_t *gu, MxT aq, hipStream_t s) {
   GemmArgs p{};
   p.C = act; p.ldc = I;
   p.C2 = gu; p.ldc2 = 2 * I;
@@ -288,13 +300,17 @@ void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_
   p.lda = H; p.ldb = H; p.sB = 2 * I * H;
   if (!mx) {
     p.A = x; p.B = W.guT;
-    launch_gemm_rows(p, EPI_SWIGLU, true, (int)max_rows, s);
+    launch_gemm_rows(p, EPI_SWIGLU, true, (int)grid_rows, s);
   } else {
     p.A = (const uint16_t *)xq.q; p.B = (const uint16_t *)W.guTq.q;
-    const MxOperands m{xq.s, W.guTq.s, (int)max_rows, aq.q, aq.s};
-    launch_gemm_rows_mx(p, m, EPI_SWIGLU, (int)max_rows, s);
+    const MxOperands m{xq.s, W.guTq.s, (int)a_rows, aq.q, aq.s};
+    launch_gemm_rows_mx(p, m, EPI_SWIGLU, (int)grid_rows, s);
   }
-  if (st) st->mark(mark);
+}
+
+void gemm_down(const uint16_t *act, MxT aq, const int32_t *offsets, const int32_t *tiles, int G,
+               long grid_rows, long a_rows, long H, long I, const WSet &W, bool mx, uint16_t *y,
+               hipStream_t s) {
   GemmArgs q{};
   q.C = y; q.ldc = H;
   q.offsets = offsets; q.tile_start = tiles;
@@ -302,26 +318,34 @@ void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_
   q.lda = I; q.ldb = I; q.sB = H * I;
   if (!mx) {
     q.A = act; q.B = W.dT;
-    launch_gemm_rows(q, EPI_BF16, true, (int)max_rows, s);
+    launch_gemm_rows(q, EPI_BF16, true, (int)grid_rows, s);
   } else {
     q.A = (const uint16_t *)aq.q; q.B = (const uint16_t *)W.dTq.q;
-    const MxOperands m{aq.s, W.dTq.s, (int)max_rows, nullptr, nullptr};
-    launch_gemm_rows_mx(q, m, EPI_BF16, (int)max_rows, s);
+    const MxOperands m{aq.s, W.dTq.s, (int)a_rows, nullptr, nullptr};
+    launch_gemm_rows_mx(q, m, EPI_BF16, (int)grid_rows, s);
   }
+}
+
+void ffn_forward(const uint16_t *x, MxT xq, const int32_t *offsets, const int32_t *tiles, int G,
+                 long max_rows, long H, long I, const WSet &W, bool mx, uint16_t *act,
+                 uint16_t *gu, MxT aq, uint16_t *y, hipStream_t s, const Stages *st = nullptr,
+                 int mark = 0) {
+  gemm_gate_up(x, xq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, act, gu, aq, s);
+  if (st) st->mark(mark);
+  gemm_down(act, aq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, y, s);
   if (st) st->mark(mark + 1);
 }
 
-// Backward of the expert FFN for row-ragged groups given dY (rows' output
-// gradient, bf16, [rows][H]).  Writes dh (packed dg|du), dX and the weight
-// gradients.  With MXFP8 the two data-gradient GEMMs consume MX copies of dY
-// and dh (quantised here into dyq, dhq); the weight gradients use the bf16
-// tensors (X and act then hold the forward's MX round trips).
-void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
-                  const int32_t *tiles, const int32_t *order, int G, long max_rows, long H,
-                  long I, const WSet &W, bool mx, MxT dyq, MxT dhq, const uint16_t *gu_saved,
-                  const uint16_t *act, uint16_t *dh, uint16_t *dX, float *dWg, float *dWu,
-                  float *dWd, hipStream_t s, const Stages *st = nullptr, int mark = 0) {
-  GemmArgs a{};  // dA = dY Wd^T, SwiGLU backward in the epilogue -> dh
+// Backward of the expert FFN, one GEMM at a time.  dA = dY Wd^T with the
+// SwiGLU backward in the epilogue -> dh (packed dg|du); dX = dh Wgu^T; the
+// weight gradients dWd = act^T dY and dWg|dWu = X^T dh.  With MXFP8 the two
+// data-gradient GEMMs consume MX copies of dY and dh (dyq, dhq, quantised by
+// the caller); the weight gradients use the bf16 tensors (X and act then hold
+// the forward's MX round trips).
+void gemm_dgrad_down(const uint16_t *dY, MxT dyq, const int32_t *offsets, const int32_t *tiles,
+                     int G, long grid_rows, long a_rows, long H, long I, const WSet &W, bool mx,
+                     const uint16_t *gu_saved, uint16_t *dh, hipStream_t s) {
+  GemmArgs a{};
   a.C = dh; a.ldc = 2 * I;
   a.aux = gu_saved; a.ldaux = 2 * I;
   a.offsets = offsets; a.tile_start = tiles;
@@ -329,44 +353,71 @@ void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
   a.lda = H; a.ldb = H; a.sB = I * H;
   if (!mx) {
     a.A = dY; a.B = W.d;
-    launch_gemm_rows(a, EPI_SWIGLU_BWD, true, (int)max_rows, s);
+    launch_gemm_rows(a, EPI_SWIGLU_BWD, true, (int)grid_rows, s);
   } else {
-    launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
     a.A = (const uint16_t *)dyq.q; a.B = (const uint16_t *)W.dq.q;
-    const MxOperands m{dyq.s, W.dq.s, (int)max_rows, nullptr, nullptr};
-    launch_gemm_rows_mx(a, m, EPI_SWIGLU_BWD, (int)max_rows, s);
+    const MxOperands m{dyq.s, W.dq.s, (int)a_rows, nullptr, nullptr};
+    launch_gemm_rows_mx(a, m, EPI_SWIGLU_BWD, (int)grid_rows, s);
   }
-  if (st) st->mark(mark);
-  GemmArgs b{};  // dWd = act^T dY
-  b.A = act; b.lda = I;
-  b.B = dY; b.ldb = H;
-  b.C = dWd; b.ldc = H; b.sC = I * H;
-  b.offsets = offsets; b.order = order;
-  b.G = G; b.M = (int)I; b.N = (int)H;
-  launch_gemm_wgrad(b, EPI_F32, s);
-  if (st) st->mark(mark + 1);
-  GemmArgs c{};  // dX = dh Wgu^T
+}
+
+void gemm_dgrad_gate_up(const uint16_t *dh, MxT dhq, const int32_t *offsets, const int32_t *tiles,
+                        int G, long grid_rows, long a_rows, long H, long I, const WSet &W,
+                        bool mx, uint16_t *dX, hipStream_t s) {
+  GemmArgs c{};
   c.C = dX; c.ldc = H;
   c.offsets = offsets; c.tile_start = tiles;
   c.G = G; c.N = (int)H; c.K = (int)(2 * I);
   c.lda = 2 * I; c.ldb = 2 * I; c.sB = H * 2 * I;
   if (!mx) {
     c.A = dh; c.B = W.gu;
-    launch_gemm_rows(c, EPI_BF16, true, (int)max_rows, s);
+    launch_gemm_rows(c, EPI_BF16, true, (int)grid_rows, s);
   } else {
-    launch_quant_rows_mx(dh, (int)max_rows, (int)(2 * I), dhq.q, dhq.s, s);
     c.A = (const uint16_t *)dhq.q; c.B = (const uint16_t *)W.guq.q;
-    const MxOperands m{dhq.s, W.guq.s, (int)max_rows, nullptr, nullptr};
-    launch_gemm_rows_mx(c, m, EPI_BF16, (int)max_rows, s);
+    const MxOperands m{dhq.s, W.guq.s, (int)a_rows, nullptr, nullptr};
+    launch_gemm_rows_mx(c, m, EPI_BF16, (int)grid_rows, s);
   }
-  if (st) st->mark(mark + 2);
-  GemmArgs e{};  // dWg | dWu = X^T dh
+}
+
+void gemm_wgrad_down(const uint16_t *act, const uint16_t *dY, const int32_t *offsets,
+                     const int32_t *order, int G, long H, long I, float *dWd, hipStream_t s) {
+  GemmArgs b{};
+  b.A = act; b.lda = I;
+  b.B = dY; b.ldb = H;
+  b.C = dWd; b.ldc = H; b.sC = I * H;
+  b.offsets = offsets; b.order = order;
+  b.G = G; b.M = (int)I; b.N = (int)H;
+  launch_gemm_wgrad(b, EPI_F32, s);
+}
+
+void gemm_wgrad_gate_up(const uint16_t *X, const uint16_t *dh, const int32_t *offsets,
+                        const int32_t *order, int G, long H, long I, float *dWg, float *dWu,
+                        hipStream_t s) {
+  GemmArgs e{};
   e.A = X; e.lda = H;
   e.B = dh; e.ldb = 2 * I;
   e.C = dWg; e.C2 = dWu; e.ldc = I; e.sC = H * I;
   e.offsets = offsets; e.order = order;
   e.G = G; e.M = (int)H; e.N = (int)(2 * I);
   launch_gemm_wgrad(e, EPI_WGRAD_GU, s);
+}
+
+// The whole expert-FFN backward over row-ragged groups, given dY (rows'
+// output gradient, bf16, [rows][H]).
+void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
+                  const int32_t *tiles, const int32_t *order, int G, long max_rows, long H,
+                  long I, const WSet &W, bool mx, MxT dyq, MxT dhq, const uint16_t *gu_saved,
+                  const uint16_t *act, uint16_t *dh, uint16_t *dX, float *dWg, float *dWu,
+                  float *dWd, hipStream_t s, const Stages *st = nullptr, int mark = 0) {
+  if (mx) launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
+  gemm_dgrad_down(dY, dyq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, gu_saved, dh, s);
+  if (st) st->mark(mark);
+  gemm_wgrad_down(act, dY, offsets, order, G, H, I, dWd, s);
+  if (st) st->mark(mark + 1);
+  if (mx) launch_quant_rows_mx(dh, (int)max_rows, (int)(2 * I), dhq.q, dhq.s, s);
+  gemm_dgrad_gate_up(dh, dhq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, dX, s);
+  if (st) st->mark(mark + 2);
+  gemm_wgrad_gate_up(X, dh, offsets, order, G, H, I, dWg, dWu, s);
   if (st) st->mark(mark + 3);
 }
 
@@ -455,6 +506,251 @@ int mk_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Save
   a.status = w.status;
   if (launch_layer_fwd_megakernel(a, cus, s)) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+// ---- pipelined schedule (MOE_SCHED_PIPELINED)
+//
+// The library's own streams and events, per device: a communication stream
+// (dispatch, combine, reverse-combine, reverse-dispatch, router gradient) and
+// two GEMM streams taking even and odd minibatches.  Every cross-stream order
+// is an event wait enqueued on the GPU; the host never waits.  An event's
+// wait is enqueued only after its record, and each call re-records the same
+// events before waiting on them, so reuse across calls is safe.
+
+static_assert(kPipeMaxMinibatches == kMkMaxMinibatches, "plan sized for the same minibatch bound");
+
+struct PipeRes {
+  bool init = false;
+  int comm_cus = -1;
+  hipStream_t comm = nullptr, gemm[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> ev;
+};
+
+std::mutex g_pipe_mu;
+PipeRes g_pipe[64];
+
+// Streams for this comm_cus on the current device (recreated when it
+// changes: a CU mask is fixed when a stream is created), and at least
+// n_events events.  Called with g_pipe_mu held.
+int pipe_resources(int comm_cus, size_t n_events, PipeRes **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  PipeRes &r = g_pipe[dev];
+  if (!r.init || r.comm_cus != comm_cus) {
+    if (r.init) {
+      // streams of an earlier comm_cus: let their work finish, then drop them
+      for (hipStream_t q : {r.comm, r.gemm[0], r.gemm[1]}) {
+        if (hipStreamSynchronize(q) != hipSuccess || hipStreamDestroy(q) != hipSuccess)
+          return MOE_ERR_HIP;
+      }
+      r.init = false;
+    }
+    const int cus = device_cus();
+    if (comm_cus > 0) {
+      if (comm_cus >= cus) return MOE_ERR_INVALID_ARG;
+      // CU mask bits: the first comm_cus bits go to the communication stream
+      // (the driver spreads consecutive mask bits over the XCDs), the rest to
+      // the GEMM streams
+      std::vector<uint32_t> cm((cus + 31) / 32, 0u), gm((cus + 31) / 32, 0u);
+      for (int i = 0; i < cus; i++) (i < comm_cus ? cm : gm)[i / 32] |= 1u << (i % 32);
+      if (hipExtStreamCreateWithCUMask(&r.comm, (uint32_t)cm.size(), cm.data()) != hipSuccess ||
+          hipExtStreamCreateWithCUMask(&r.gemm[0], (uint32_t)gm.size(), gm.data()) !=
+              hipSuccess ||
+          hipExtStreamCreateWithCUMask(&r.gemm[1], (uint32_t)gm.size(), gm.data()) != hipSuccess)
+        return MOE_ERR_HIP;
+    } else {
+      for (hipStream_t *q : {&r.comm, &r.gemm[0], &r.gemm[1]})
+        if (hipStreamCreateWithFlags(q, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+    }
+    r.comm_cus = comm_cus;
+    r.init = true;
+  }
+  while (r.ev.size() < n_events) {
+    hipEvent_t e;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return MOE_ERR_HIP;
+    r.ev.push_back(e);
+  }
+  *out = &r;
+  return MOE_OK;
+}
+
+// Rows per minibatch: the caller's, else enough for two full waves of the
+// gate/up GEMM's 256 x 256 tiles [KC §02: at least two waves]; never below
+// the plan's bound.
+long pipe_minibatch(const Dims &d, const moe_sched *sc) {
+  long mb = sc->minibatch_rows;
+  if (mb <= 0) {
+    const long n_tiles = (2 * d.I + kTileN - 1) / kTileN;
+    const long row_tiles = (2L * std::max(device_cus(), 1) + n_tiles - 1) / n_tiles;
+    mb = row_tiles * kTileM;
+  }
+  return std::min(std::max(mb, mk_min_minibatch(d)), d.R);
+}
+
+struct PipeCtx {
+  PipeRes *r;
+  hipStream_t s;
+  bool wait(hipStream_t q, int e) const { return hipStreamWaitEvent(q, r->ev[e], 0) == hipSuccess; }
+  bool rec(hipStream_t q, int e) const { return hipEventRecord(r->ev[e], q) == hipSuccess; }
+  // caller's stream -> all three streams
+  bool fork(int e) const {
+    return rec(s, e) && wait(r->comm, e) && wait(r->gemm[0], e) && wait(r->gemm[1], e);
+  }
+  // all three streams -> caller's stream (events e, e+1, e+2)
+  bool join(int e) const {
+    return rec(r->comm, e) && rec(r->gemm[0], e + 1) && rec(r->gemm[1], e + 2) && wait(s, e) &&
+           wait(s, e + 1) && wait(s, e + 2);
+  }
+};
+
+// Forward after routing and layout: dispatch, gate/up + SwiGLU, down, shared
+// expert and combine, minibatch by minibatch.
+//   comm   : D(0) .. D(S-1), then D(m+S), C(m) for m = 0, 1, ...
+//   gemm[m%2]: G(m) = gate/up(m), down(m)     (shared expert first, on gemm[0])
+// D(m+S) waits for gate/up(m) (at most S minibatches dispatched ahead: the
+// pages' ring of S slots read as an in-flight window; the rows stay in the
+// forward context for the backward); G(m) waits for D(m); C(m) waits for
+// down(m) and down(m-1), which with the two GEMM streams' own order covers
+// every earlier minibatch and the shared expert.
+int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Saved &sv,
+                 const Packed &p, const Work &w, uint16_t *out, hipStream_t s) {
+  const long MB = pipe_minibatch(d, sc);
+  const int NM = (int)((d.R + MB - 1) / MB);
+  if (NM > w.max_nm) return MOE_ERR_INVALID_ARG;
+  const int S = sc->ring_slots > 0 ? sc->ring_slots : 2;
+  const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k, R = (int)d.R;
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  PipeRes *r = nullptr;
+  int rc = pipe_resources(sc->comm_cus, 3 * (size_t)NM + 4, &r);
+  if (rc) return rc;
+  const int evD = 0, evG1 = NM, evG2 = 2 * NM, evX = 3 * NM;
+  const PipeCtx c{r, s};
+  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
+                   w.tlf_off, w.tlb, w.tlb_off, s);
+  if (!c.fork(evX)) return MOE_ERR_HIP;
+  if (d.shared) {
+    hipStream_t q = r->gemm[0];
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, q);
+    if (d.mx) launch_dispatch_mx(x, nullptr, sv.xq_s.q, sv.xq_s.s, sv.xhat_s, T, 1, H, q);
+    ffn_forward(x, sv.xq_s, w.dense_offsets, w.dense_tiles, 1, d.T, d.H, d.Is, p.s, d.mx,
+                sv.act_s, sv.gu_s, sv.aq_s, sv.y_s, q);
+  }
+  auto rows_of = [&](int m) { return (int)std::min(MB, d.R - (long)m * MB); };
+  auto D = [&](int m) {
+    const int r0 = (int)(m * MB), n = rows_of(m);
+    if (m >= S && !c.wait(r->comm, evG1 + m - S)) return false;
+    if (d.mx)
+      launch_dispatch_mx_range(x, sv.perm, sv.xq.q, sv.xq.s, sv.x_perm, r0, n, R, k, H, r->comm);
+    else
+      launch_dispatch_bf16(x, sv.perm + r0, sv.x_perm + (size_t)r0 * H, n, k, H, r->comm);
+    return c.rec(r->comm, evD + m);
+  };
+  auto G = [&](int m) {
+    hipStream_t q = r->gemm[m & 1];
+    const int32_t *mo = w.pm_off + (size_t)m * (E + 1), *mt = w.pm_ts + (size_t)m * (E + 1);
+    if (!c.wait(q, evD + m)) return false;
+    gemm_gate_up(sv.x_perm, sv.xq, mo, mt, E, rows_of(m), d.R, d.H, d.I, p.r, d.mx, sv.act, sv.gu,
+                 sv.aq, q);
+    if (!c.rec(q, evG1 + m)) return false;
+    gemm_down(sv.act, sv.aq, mo, mt, E, rows_of(m), d.R, d.H, d.I, p.r, d.mx, sv.y, q);
+    return c.rec(q, evG2 + m);
+  };
+  auto C = [&](int m) {
+    if (!c.wait(r->comm, evG2 + m) || (m > 0 && !c.wait(r->comm, evG2 + m - 1))) return false;
+    launch_combine_list(sv.y, sv.w, sv.inv, d.shared ? sv.y_s : nullptr, out, w.tlf, w.tlf_off, m,
+                        T, k, H, r->comm);
+    return true;
+  };
+  for (int m = 0; m < std::min(S, NM); m++)
+    if (!D(m)) return MOE_ERR_HIP;
+  for (int m = 0; m < NM; m++) {
+    if (!G(m)) return MOE_ERR_HIP;
+    if (m + S < NM && !D(m + S)) return MOE_ERR_HIP;
+    if (!C(m)) return MOE_ERR_HIP;
+  }
+  if (!c.join(evX + 1)) return MOE_ERR_HIP;
+  return hip_status();
+}
+
+// Backward, minibatches in reverse [NA design]:
+//   comm   : RC(NM-1), then RC(m-1), RD(m) for m = NM-1 .. 0, then the
+//            router's weight gradient
+//   gemm[i%2] (i-th minibatch of the walk): dgrad-down + SwiGLU bwd(m),
+//            dgrad-gate/up(m)   (shared expert's whole backward first, on
+//            gemm[0])
+//   gemm[0] at the end: both weight gradients over all rows.
+// RC = reverse-combine of minibatch m's rows; RD(m) = reverse-dispatch of the
+// tokens whose first routed row lies in minibatch m (all their row gradients
+// are done once the walk has passed m).  Nothing is replayed: the forward
+// context holds every row's g|u (288 GB of HBM leaves room for it).
+int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, const uint16_t *x,
+                  const uint16_t *w_router, const Saved &sv, const Packed &p, const Work &w, uint16_t *dx,
+                  float *dw_router, float *dw_gate, float *dw_up, float *dw_down, float *dws,
+                  float *dw, hipStream_t s) {
+  const long MB = pipe_minibatch(d, sc);
+  const int NM = (int)((d.R + MB - 1) / MB);
+  if (NM > w.max_nm) return MOE_ERR_INVALID_ARG;
+  const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k, R = (int)d.R;
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  PipeRes *r = nullptr;
+  int rc = pipe_resources(sc->comm_cus, 2 * (size_t)NM + 4, &r);
+  if (rc) return rc;
+  const int evRC = 0, evDG = NM, evX = 2 * NM;
+  const PipeCtx c{r, s};
+  const bool router = w_router != nullptr;
+  if (router) launch_transpose_pack(w_router, w.wrT, 1, H, E, E, 32, 0, s);
+  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
+                   w.tlf_off, w.tlb, w.tlb_off, s);
+  if (!c.fork(evX)) return MOE_ERR_HIP;
+  if (d.shared) {
+    hipStream_t q = r->gemm[0];
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, q);
+    float *dWsg = dws, *dWsu = dws + d.H * d.Is, *dWsd = dws + 2 * d.H * d.Is;
+    ffn_backward(d.mx ? sv.xhat_s : x, dout, w.dense_offsets, w.dense_tiles, w.dense_order, 1,
+                 d.T, d.H, d.Is, p.s, d.mx, w.doutq, w.dhq_s, sv.gu_s, sv.act_s, w.dh_s, w.dxs,
+                 dWsg, dWsu, dWsd, q);
+  }
+  auto rows_of = [&](int m) { return (int)std::min(MB, d.R - (long)m * MB); };
+  auto RC = [&](int m) {
+    launch_reverse_combine_rows(dout, sv.y, sv.w, sv.perm, w.dy, dw, (int)(m * MB), rows_of(m), k,
+                                H, r->comm);
+    return c.rec(r->comm, evRC + m);
+  };
+  auto DG = [&](int m, hipStream_t q) {
+    const int r0 = (int)(m * MB), n = rows_of(m);
+    const int32_t *mo = w.pm_off + (size_t)m * (E + 1), *mt = w.pm_ts + (size_t)m * (E + 1);
+    if (!c.wait(q, evRC + m)) return false;
+    if (d.mx) launch_quant_rows_mx_range(w.dy, r0, n, R, H, w.dyq.q, w.dyq.s, q);
+    gemm_dgrad_down(w.dy, w.dyq, mo, mt, E, n, d.R, d.H, d.I, p.r, d.mx, sv.gu, w.dh, q);
+    if (d.mx) launch_quant_rows_mx_range(w.dh, r0, n, R, (int)(2 * d.I), w.dhq.q, w.dhq.s, q);
+    gemm_dgrad_gate_up(w.dh, w.dhq, mo, mt, E, n, d.R, d.H, d.I, p.r, d.mx, w.dX, q);
+    return c.rec(q, evDG + m);
+  };
+  auto RD = [&](int m) {
+    if (!c.wait(r->comm, evDG + m) || (m + 1 < NM && !c.wait(r->comm, evDG + m + 1)))
+      return false;
+    launch_reverse_dispatch_list(w.dX, sv.inv, sv.idx, sv.w, dw, w.dsel,
+                                 router ? w.wrT : nullptr, d.shared ? w.dxs : nullptr, dx, w.tlb,
+                                 w.tlb_off, m, T, k, H, r->comm);
+    return true;
+  };
+  if (!RC(NM - 1)) return MOE_ERR_HIP;
+  for (int i = 0; i < NM; i++) {
+    const int m = NM - 1 - i;
+    if (!DG(m, r->gemm[i & 1])) return MOE_ERR_HIP;
+    if (m > 0 && !RC(m - 1)) return MOE_ERR_HIP;
+    if (!RD(m)) return MOE_ERR_HIP;
+  }
+  if (router) launch_router_wgrad(x, sv.perm, sv.offsets, w.dsel, dw_router, E, k, H, r->comm);
+  // weight gradients over all rows: every dY (reverse-combine, in order on
+  // comm) and every dh (the walk's last two minibatches, one per GEMM stream)
+  hipStream_t q = r->gemm[0];
+  if (!c.wait(q, evRC + 0) || !c.wait(q, evDG + 0) || (NM > 1 && !c.wait(q, evDG + 1)))
+    return MOE_ERR_HIP;
+  gemm_wgrad_down(sv.act, w.dy, sv.offsets, sv.order, E, d.H, d.I, dw_down, q);
+  gemm_wgrad_gate_up(sv.x_perm, w.dh, sv.offsets, sv.order, E, d.H, d.I, dw_gate, dw_up, q);
+  if (!c.join(evX + 1)) return MOE_ERR_HIP;
+  return hip_status();
 }
 
 }  // namespace
@@ -637,7 +933,11 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
     return MOE_ERR_INVALID_ARG;
   if (router && (d.k > d.E)) return MOE_ERR_INVALID_ARG;
   if (router && d.E % 8) return MOE_ERR_UNSUPPORTED;
-  if (sched && sched->use_megakernel && !kMegakernelEnabled) return MOE_ERR_UNSUPPORTED;
+  const int mode = sched ? sched->schedule : MOE_SCHED_STAGED;
+  if (mode != MOE_SCHED_STAGED && mode != MOE_SCHED_PERSISTENT && mode != MOE_SCHED_PIPELINED)
+    return MOE_ERR_INVALID_ARG;
+  if (mode == MOE_SCHED_PERSISTENT && !kMegakernelEnabled) return MOE_ERR_UNSUPPORTED;
+  if (mode == MOE_SCHED_PIPELINED && sched->comm_cus < 0) return MOE_ERR_INVALID_ARG;
   Work w;
   if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
   Saved sv;
@@ -672,11 +972,17 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   launch_layout(sv.idx, (int)d.R, E, w.chunk_counts, sv.counts, sv.offsets, sv.perm, sv.inv,
                 sv.tile_start, kTileM, sv.order, s);
   st.mark(1);
-  if (sched && sched->use_megakernel) {
+  if (mode == MOE_SCHED_PERSISTENT) {
     // The persistent forward is switched off: its first GPU runs did not
     // finish (the cause is not yet found), so it is refused rather than run.
     if (!kMegakernelEnabled) return MOE_ERR_UNSUPPORTED;
     rc = mk_forward(d, sched, x, sv, p, w, out, s);
+    if (rc) return rc;
+    for (int i = 2; i <= 6; i++) st.mark(i);
+    return hip_status();
+  }
+  if (mode == MOE_SCHED_PIPELINED) {
+    rc = pipe_forward(d, sched, x, sv, p, w, out, s);
     if (rc) return rc;
     for (int i = 2; i <= 6; i++) st.mark(i);
     return hip_status();
@@ -717,6 +1023,10 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   const bool router = w_router != nullptr;
   if (router && !dw_router) return MOE_ERR_INVALID_ARG;
   if (d.shared && !dws) return MOE_ERR_INVALID_ARG;
+  const int mode = sched ? sched->schedule : MOE_SCHED_STAGED;
+  if (mode != MOE_SCHED_STAGED && mode != MOE_SCHED_PERSISTENT && mode != MOE_SCHED_PIPELINED)
+    return MOE_ERR_INVALID_ARG;
+  if (mode == MOE_SCHED_PIPELINED && sched->comm_cus < 0) return MOE_ERR_INVALID_ARG;
   Work w;
   if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
   Saved sv;
@@ -728,9 +1038,16 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   const Stages st{sched, s};
   st.mark(0);
   launch_fill_i32(w.status, 1, MOE_OK, s);
+  float *dw = dtopk_w ? dtopk_w : w.dw;
+  if (mode == MOE_SCHED_PIPELINED) {
+    rc = pipe_backward(d, sched, dout, x, w_router, sv, p, w, dx, dw_router, dw_gate, dw_up,
+                       dw_down, dws, dw, s);
+    if (rc) return rc;
+    for (int i = 1; i <= 7; i++) st.mark(i);
+    return hip_status();
+  }
 
   // Reverse-combine: dY rows, dw, and (router) the selected-logit gradient
-  float *dw = dtopk_w ? dtopk_w : w.dw;
   launch_reverse_combine(dout, sv.y, sv.w, sv.inv, w.dy, dw, router ? w.dsel : nullptr, T, k, H,
                          s);
   st.mark(1);

@@ -11,6 +11,8 @@ constexpr int kLayoutChunk = 1024;  // flat rows per block of the layout passes
 constexpr int kTileM = 256;         // rows of one grouped-GEMM tile
 constexpr int kTileN = 256;         // columns of one grouped-GEMM tile
 constexpr int kTileK = 64;          // contraction depth of one LDS stage
+constexpr int kPipeMaxMinibatches = 1024;  // minibatches of one pipelined call, at most
+constexpr int kMaxTopKList = 16;    // top-k bound of the token-list kernels
 
 // route_layout.hip
 void launch_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w,
@@ -36,6 +38,12 @@ void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq,
                              uint16_t *xhat, int T, int k, int H, hipStream_t s);
 void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
                           hipStream_t s);
+// Rows [row0, row0 + rows) of a matrix of rows_total rows (scale plane stride).
+void launch_dispatch_mx_range(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
+                              uint16_t *xhat, int row0, int rows, int rows_total, int k, int H,
+                              hipStream_t s);
+void launch_quant_rows_mx_range(const uint16_t *src, int row0, int rows, int rows_total, int cols,
+                                uint8_t *q, uint8_t *sc, hipStream_t s);
 void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,
                     uint16_t *out, int T, int k, int H, hipStream_t s);
 void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float *w,
@@ -50,6 +58,22 @@ void launch_transpose_pack(const uint16_t *in, uint16_t *out, int G, int rows, i
                            int out_rows_total, int blk_stride, int blk_off, hipStream_t s);
 void launch_interleave_copy(const uint16_t *in, uint16_t *out, int G, int rows, int cols,
                             int out_cols, int blk_stride, int blk_off, hipStream_t s);
+
+// pipeline.hip: the minibatch schedule's plan and its per-minibatch data movement
+void launch_pipe_plan(const int32_t *offsets, const int32_t *inv, int T, int k, int E, int R,
+                      int MB, int NM, int32_t *moff, int32_t *mts, int32_t *tlf, int32_t *tlf_off,
+                      int32_t *tlb, int32_t *tlb_off, hipStream_t s);
+void launch_combine_list(const uint16_t *y, const float *w, const int32_t *inv,
+                         const uint16_t *ys, uint16_t *out, const int32_t *tl,
+                         const int32_t *tl_off, int m, int T, int k, int H, hipStream_t s);
+void launch_reverse_combine_rows(const uint16_t *dout, const uint16_t *y, const float *w,
+                                 const int32_t *perm, uint16_t *dy, float *dw, int r0, int rows,
+                                 int k, int H, hipStream_t s);
+void launch_reverse_dispatch_list(const uint16_t *dX, const int32_t *inv, const int32_t *idx,
+                                  const float *w, const float *dw, float *dsel,
+                                  const uint16_t *wrT, const uint16_t *dxs, uint16_t *dx,
+                                  const int32_t *tl, const int32_t *tl_off, int m, int T, int k,
+                                  int H, hipStream_t s);
 
 // gemm.hip: grouped GEMMs on MFMA (bf16 inputs, fp32 accumulation)
 enum EpiKind { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_WGRAD_GU = 4 };

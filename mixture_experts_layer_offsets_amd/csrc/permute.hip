@@ -68,12 +68,15 @@ void launch_dispatch_bf16(const uint16_t *x, const int32_t *perm, uint16_t *xp, 
 // exchanges), so loads and stores are contiguous across the wave.  Writes the
 // E4M3 codes, the E8M0 scales and (if xhat) the dequantised row as bf16.
 // The grid covers whole quads: R * H/8 is a multiple of 4.
+// Rows [row0, row0 + R) of an output of `rows_total` rows (the scale plane's
+// row stride), so one minibatch of sorted rows can be converted on its own.
 __global__ __launch_bounds__(256) void dispatch_mx_kernel(
     const uint4 *__restrict__ x, const int32_t *__restrict__ perm, uint2 *__restrict__ xq,
-    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int R, int k, int HC /* H/8 */) {
+    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int row0, int R, long rows_total, int k,
+    int HC /* H/8 */) {
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
   if (id >= (long)R * HC) return;
-  const int r = (int)(id / HC), c = (int)(id - (long)r * HC);
+  const int r = row0 + (int)(id / HC), c = (int)(id - (long)(r - row0) * HC);
   const int src_row = perm ? perm[r] / k : r;
   float v[8];
   unpack8(x[(size_t)src_row * HC + c], v);
@@ -81,17 +84,24 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(
   float deq[8];
   const uint32_t sc = mx_quad8(v, &codes, deq);
   xq[(size_t)r * HC + c] = codes;
-  // scales K-blocked: block b = c/4 of row r at byte (b/4 * R + r) * 4 + b%4
-  if ((c & 3) == 0) xs[((size_t)(c >> 4) * R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
+  // scales K-blocked: block b = c/4 of row r at byte (b/4 * rows_total + r) * 4 + b%4
+  if ((c & 3) == 0) xs[((size_t)(c >> 4) * rows_total + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
   if (xhat) xhat[(size_t)r * HC + c] = pack8(deq);
+}
+
+void launch_dispatch_mx_range(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
+                              uint16_t *xhat, int row0, int rows, int rows_total, int k, int H,
+                              hipStream_t s) {
+  const long n = (long)rows * (H / 8);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const uint4 *)x, perm, (uint2 *)xq, xs, (uint4 *)xhat, row0, rows,
+                     (long)rows_total, k, H / 8);
 }
 
 void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uint8_t *xs,
                         uint16_t *xhat, int R, int k, int H, hipStream_t s) {
-  const long n = (long)R * (H / 8);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const uint4 *)x, perm, (uint2 *)xq, xs, (uint4 *)xhat, R, k, H / 8);
+  launch_dispatch_mx_range(x, perm, xq, xs, xhat, 0, R, R, k, H, s);
 }
 
 // Dispatch in scatter form, for the layer (which has inv = perm^-1): token
@@ -163,11 +173,12 @@ void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq,
 // Row-wise MX quantisation of a bf16 matrix along its contiguous axis.
 void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
                           hipStream_t s) {
-  const long n = (long)rows * (cols / 8);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(dispatch_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const uint4 *)src, (const int32_t *)nullptr, (uint2 *)q, sc,
-                     (uint4 *)nullptr, rows, 1, cols / 8);
+  launch_dispatch_mx_range(src, nullptr, q, sc, nullptr, 0, rows, rows, 1, cols, s);
+}
+
+void launch_quant_rows_mx_range(const uint16_t *src, int row0, int rows, int rows_total, int cols,
+                                uint8_t *q, uint8_t *sc, hipStream_t s) {
+  launch_dispatch_mx_range(src, nullptr, q, sc, nullptr, row0, rows, rows_total, 1, cols, s);
 }
 
 // ---------------------------------------------------------------------------

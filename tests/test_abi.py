@@ -149,7 +149,7 @@ def test_megakernel_request_is_refused(lib):
     MOE_ERR_UNSUPPORTED before any device work."""
     s = ctypes.byref(m.Shape(64, 128, 8, 2, 64).c())
     sched = m.MoeSched()
-    sched.use_megakernel = 1
+    sched.schedule = 1
     fake = 1 << 40
     assert lib.moe_layer_fwd(s, ctypes.byref(sched), fake, None, None, fake, fake, fake, fake,
                              fake, fake, 1 << 40, None) == _lib.MOE_ERR_UNSUPPORTED

@@ -1,4 +1,4 @@
-"""The persistent pipelined forward (moe_sched.use_megakernel = 1) against the
+"""The persistent pipelined forward (moe_sched.schedule = 1) against the
 staged forward and the oracle.
 
 The persistent kernel runs the same tile, dispatch and combine arithmetic as
@@ -84,7 +84,7 @@ class Pair:
 
 def mk_sched(**kw):
     s = m.MoeSched()
-    s.use_megakernel = 1
+    s.schedule = 1
     for k, v in kw.items():
         setattr(s, k, v)
     return s
