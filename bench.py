@@ -7,8 +7,15 @@ line.  The default workload is the Kimi-shaped expert share: 2048 tokens x
 top-8 = 16,384 routed rows, hidden 7168, 6 local experts of intermediate 2048,
 Zipf(s=1.0) expert loads, bf16.
 
+Both schedules of the layer are timed: the staged one (one kernel per step
+over all rows) and the minibatch-pipelined one (communication and GEMM
+streams); `value` is the throughput of --schedule (default: pipelined).  The
+per-stage times, MFMA and HBM fractions and the roofline come from a staged
+pass with HIP events around every kernel on the layer's stream.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--schedule staged|pipelined] [--minibatch-rows N]
+                    [--comm-cus N] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -53,7 +60,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the bounded oracle sample (CPU baseline)")
-    ap.add_argument("--schedule", choices=("staged", "pipelined"), default="staged",
+    ap.add_argument("--schedule", choices=("staged", "pipelined"), default="pipelined",
                     help="schedule whose throughput is `value` (both are timed and reported)")
     ap.add_argument("--minibatch-rows", type=int, default=0,
                     help="pipelined schedule: routed rows per minibatch (0 = library default)")

@@ -574,13 +574,22 @@ int pipe_resources(int comm_cus, size_t n_events, PipeRes **out) {
   return MOE_OK;
 }
 
-// Rows per minibatch: the caller's, else enough for two full waves of the
-// gate/up GEMM's 256 x 256 tiles [KC §02: at least two waves]; never below
-// the plan's bound.
-long pipe_minibatch(const Dims &d, const moe_sched *sc) {
+// Rows per minibatch: the caller's, else
+//  - backward: enough rows for two full waves of 256 x 256 tiles of its first
+//    GEMM (the down data gradient, I columns) [KC §02: a minibatch should fill
+//    the compute units at least twice];
+//  - forward (fwd = true): all rows.  Measured on MI355X at the Kimi-shaped
+//    share: with two minibatches the forward is ~0.1 ms slower than one
+//    pass -- on one GPU dispatch and combine are HBM copies of ~50 us each,
+//    there is little to hide, and every cross-stream hand-off adds latency;
+//    the backward gains from running its weight gradients beside the data
+//    gradients.
+// Never below the plan's bound.
+long pipe_minibatch(const Dims &d, const moe_sched *sc, bool fwd) {
   long mb = sc->minibatch_rows;
   if (mb <= 0) {
-    const long n_tiles = (2 * d.I + kTileN - 1) / kTileN;
+    if (fwd) return d.R;
+    const long n_tiles = (d.I + kTileN - 1) / kTileN;
     const long row_tiles = (2L * std::max(device_cus(), 1) + n_tiles - 1) / n_tiles;
     mb = row_tiles * kTileM;
   }
@@ -614,7 +623,7 @@ struct PipeCtx {
 // every earlier minibatch and the shared expert.
 int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Saved &sv,
                  const Packed &p, const Work &w, uint16_t *out, hipStream_t s) {
-  const long MB = pipe_minibatch(d, sc);
+  const long MB = pipe_minibatch(d, sc, true);
   const int NM = (int)((d.R + MB - 1) / MB);
   if (NM > w.max_nm) return MOE_ERR_INVALID_ARG;
   const int S = sc->ring_slots > 0 ? sc->ring_slots : 2;
@@ -639,10 +648,13 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
   auto D = [&](int m) {
     const int r0 = (int)(m * MB), n = rows_of(m);
     if (m >= S && !c.wait(r->comm, evG1 + m - S)) return false;
+    // token-driven, writing only this minibatch's rows: every token is read
+    // once per minibatch, not once per routed row
     if (d.mx)
-      launch_dispatch_mx_range(x, sv.perm, sv.xq.q, sv.xq.s, sv.x_perm, r0, n, R, k, H, r->comm);
+      launch_dispatch_push_mx_range(x, sv.inv, sv.xq.q, sv.xq.s, sv.x_perm, T, k, H, r0, r0 + n,
+                                    r->comm);
     else
-      launch_dispatch_bf16(x, sv.perm + r0, sv.x_perm + (size_t)r0 * H, n, k, H, r->comm);
+      launch_dispatch_push_bf16_range(x, sv.inv, sv.x_perm, T, k, H, r0, r0 + n, r->comm);
     return c.rec(r->comm, evD + m);
   };
   auto G = [&](int m) {
@@ -673,27 +685,30 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
 }
 
 // Backward, minibatches in reverse [NA design]:
-//   comm   : RC(NM-1), then RC(m-1), RD(m) for m = NM-1 .. 0, then the
-//            router's weight gradient
-//   gemm[i%2] (i-th minibatch of the walk): dgrad-down + SwiGLU bwd(m),
-//            dgrad-gate/up(m)   (shared expert's whole backward first, on
-//            gemm[0])
-//   gemm[0] at the end: both weight gradients over all rows.
+//   comm    : RC(NM-1), then RC(m-1), RD(m) for m = NM-1 .. 0, then the
+//             router's weight gradient
+//   gemm[0] : the shared expert's whole backward, then for m = NM-1 .. 0:
+//             dgrad-down + SwiGLU bwd(m), dgrad-gate/up(m)
+//   gemm[1] : the down weight gradient over all rows once every dY is
+//             written (after RC(0)), then the gate/up weight gradient once
+//             every dh is (after the last dgrad-down)
 // RC = reverse-combine of minibatch m's rows; RD(m) = reverse-dispatch of the
 // tokens whose first routed row lies in minibatch m (all their row gradients
-// are done once the walk has passed m).  Nothing is replayed: the forward
+// are done once the walk has passed m).  The weight gradients run beside the
+// data-gradient walk, so each fills the compute units the other's last,
+// partly filled round of tiles leaves idle.  Nothing is replayed: the forward
 // context holds every row's g|u (288 GB of HBM leaves room for it).
 int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, const uint16_t *x,
                   const uint16_t *w_router, const Saved &sv, const Packed &p, const Work &w, uint16_t *dx,
                   float *dw_router, float *dw_gate, float *dw_up, float *dw_down, float *dws,
                   float *dw, hipStream_t s) {
-  const long MB = pipe_minibatch(d, sc);
+  const long MB = pipe_minibatch(d, sc, false);
   const int NM = (int)((d.R + MB - 1) / MB);
   if (NM > w.max_nm) return MOE_ERR_INVALID_ARG;
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k, R = (int)d.R;
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes *r = nullptr;
-  int rc = pipe_resources(sc->comm_cus, 2 * (size_t)NM + 4, &r);
+  int rc = pipe_resources(sc->comm_cus, 2 * (size_t)NM + 5, &r);
   if (rc) return rc;
   const int evRC = 0, evDG = NM, evX = 2 * NM;
   const PipeCtx c{r, s};
@@ -716,38 +731,38 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
                                 H, r->comm);
     return c.rec(r->comm, evRC + m);
   };
+  const int evDD = 2 * NM + 4;  // dgrad-down of the walk's last minibatch
   auto DG = [&](int m, hipStream_t q) {
     const int r0 = (int)(m * MB), n = rows_of(m);
     const int32_t *mo = w.pm_off + (size_t)m * (E + 1), *mt = w.pm_ts + (size_t)m * (E + 1);
     if (!c.wait(q, evRC + m)) return false;
     if (d.mx) launch_quant_rows_mx_range(w.dy, r0, n, R, H, w.dyq.q, w.dyq.s, q);
     gemm_dgrad_down(w.dy, w.dyq, mo, mt, E, n, d.R, d.H, d.I, p.r, d.mx, sv.gu, w.dh, q);
+    if (m == 0 && !c.rec(q, evDD)) return false;
     if (d.mx) launch_quant_rows_mx_range(w.dh, r0, n, R, (int)(2 * d.I), w.dhq.q, w.dhq.s, q);
     gemm_dgrad_gate_up(w.dh, w.dhq, mo, mt, E, n, d.R, d.H, d.I, p.r, d.mx, w.dX, q);
     return c.rec(q, evDG + m);
   };
   auto RD = [&](int m) {
-    if (!c.wait(r->comm, evDG + m) || (m + 1 < NM && !c.wait(r->comm, evDG + m + 1)))
-      return false;
+    if (!c.wait(r->comm, evDG + m)) return false;
     launch_reverse_dispatch_list(w.dX, sv.inv, sv.idx, sv.w, dw, w.dsel,
                                  router ? w.wrT : nullptr, d.shared ? w.dxs : nullptr, dx, w.tlb,
                                  w.tlb_off, m, T, k, H, r->comm);
     return true;
   };
   if (!RC(NM - 1)) return MOE_ERR_HIP;
-  for (int i = 0; i < NM; i++) {
-    const int m = NM - 1 - i;
-    if (!DG(m, r->gemm[i & 1])) return MOE_ERR_HIP;
+  for (int m = NM - 1; m >= 0; m--) {
+    if (!DG(m, r->gemm[0])) return MOE_ERR_HIP;
     if (m > 0 && !RC(m - 1)) return MOE_ERR_HIP;
     if (!RD(m)) return MOE_ERR_HIP;
   }
   if (router) launch_router_wgrad(x, sv.perm, sv.offsets, w.dsel, dw_router, E, k, H, r->comm);
-  // weight gradients over all rows: every dY (reverse-combine, in order on
-  // comm) and every dh (the walk's last two minibatches, one per GEMM stream)
-  hipStream_t q = r->gemm[0];
-  if (!c.wait(q, evRC + 0) || !c.wait(q, evDG + 0) || (NM > 1 && !c.wait(q, evDG + 1)))
-    return MOE_ERR_HIP;
+  // weight gradients over all rows, beside the walk: every dY is written once
+  // RC(0) is (in order on comm), every dh once the walk's last dgrad-down is
+  hipStream_t q = r->gemm[1];
+  if (!c.wait(q, evRC + 0)) return MOE_ERR_HIP;
   gemm_wgrad_down(sv.act, w.dy, sv.offsets, sv.order, E, d.H, d.I, dw_down, q);
+  if (!c.wait(q, evDD)) return MOE_ERR_HIP;
   gemm_wgrad_gate_up(sv.x_perm, w.dh, sv.offsets, sv.order, E, d.H, d.I, dw_gate, dw_up, q);
   if (!c.join(evX + 1)) return MOE_ERR_HIP;
   return hip_status();
@@ -981,7 +996,9 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
     for (int i = 2; i <= 6; i++) st.mark(i);
     return hip_status();
   }
-  if (mode == MOE_SCHED_PIPELINED) {
+  // a one-minibatch pipelined forward is the staged forward: it runs below,
+  // on the caller's stream
+  if (mode == MOE_SCHED_PIPELINED && pipe_minibatch(d, sched, true) < d.R) {
     rc = pipe_forward(d, sched, x, sv, p, w, out, s);
     if (rc) return rc;
     for (int i = 2; i <= 6; i++) st.mark(i);

@@ -36,6 +36,12 @@ void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *
                                int H, hipStream_t s);
 void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq, uint8_t *xs,
                              uint16_t *xhat, int T, int k, int H, hipStream_t s);
+// ... writing only the sorted rows in [r0, r1) (one minibatch)
+void launch_dispatch_push_bf16_range(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T,
+                                     int k, int H, int r0, int r1, hipStream_t s);
+void launch_dispatch_push_mx_range(const uint16_t *x, const int32_t *inv, uint8_t *xq,
+                                   uint8_t *xs, uint16_t *xhat, int T, int k, int H, int r0,
+                                   int r1, hipStream_t s);
 void launch_quant_rows_mx(const uint16_t *src, int rows, int cols, uint8_t *q, uint8_t *sc,
                           hipStream_t s);
 // Rows [row0, row0 + rows) of a matrix of rows_total rows (scale plane stride).

@@ -109,42 +109,63 @@ void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uin
 // sorted rows inv[t*k + j].  Same result as the gather above; it reads each
 // token once instead of k times.  Grid (H/8 chunks over 128 threads, T).
 
+// Only rows in [r0, r1) are written (one minibatch of sorted rows; the whole
+// set is [0, T*k)).
 __global__ __launch_bounds__(128) void dispatch_push_bf16_kernel(const uint4 *__restrict__ x,
                                                                  const int32_t *__restrict__ inv,
                                                                  uint4 *__restrict__ xp, int k,
-                                                                 int HC) {
+                                                                 int HC, int r0, int r1) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * 128 + threadIdx.x;
   if (c >= HC) return;
   int row[kMaxTopKPush];
+  bool any = false;
 #pragma unroll
-  for (int j = 0; j < kMaxTopKPush; j++) row[j] = inv[t * k + min(j, k - 1)];
+  for (int j = 0; j < kMaxTopKPush; j++) {
+    row[j] = inv[t * k + min(j, k - 1)];
+    any |= j < k && row[j] >= r0 && row[j] < r1;
+  }
+  if (!any) return;
   const uint4 v = x[(size_t)t * HC + c];
 #pragma unroll
   for (int j = 0; j < kMaxTopKPush; j++)
-    if (j < k) xp[(size_t)row[j] * HC + c] = v;
+    if (j < k && row[j] >= r0 && row[j] < r1) xp[(size_t)row[j] * HC + c] = v;
+}
+
+void launch_dispatch_push_bf16_range(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T,
+                                     int k, int H, int r0, int r1, hipStream_t s) {
+  const int HC = H / 8;
+  if (T <= 0) return;
+  hipLaunchKernelGGL(dispatch_push_bf16_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
+                     (const uint4 *)x, inv, (uint4 *)xp, k, HC, r0, r1);
 }
 
 void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T, int k,
                                int H, hipStream_t s) {
-  const int HC = H / 8;
-  if (T <= 0) return;
-  hipLaunchKernelGGL(dispatch_push_bf16_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
-                     (const uint4 *)x, inv, (uint4 *)xp, k, HC);
+  launch_dispatch_push_bf16_range(x, inv, xp, T, k, H, 0, T * k, s);
 }
 
 // MX: each lane quantises 8 values as in dispatch_mx_kernel (a quad of lanes
 // per 32-value block), then stores codes, scale and round trip to k rows.
+// Only rows in [r0, r1) are written.  Whether a token has such a row is the
+// same for the four lanes of a quad (one token), so the quad's block-maximum
+// exchange never mixes a returning lane with a working one.
 __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
     const uint4 *__restrict__ x, const int32_t *__restrict__ inv, uint2 *__restrict__ xq,
-    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int T, int k, int HC /* H/8 */) {
+    uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int T, int k, int HC /* H/8 */, int r0,
+    int r1) {
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
   if (id >= (long)T * HC) return;
   const long R = (long)T * k;  // rows of the output (scale plane stride)
   const int t = (int)(id / HC), c = (int)(id - (long)t * HC);
   int row[kMaxTopKPush];
+  bool any = false;
 #pragma unroll
-  for (int j = 0; j < kMaxTopKPush; j++) row[j] = inv[t * k + min(j, k - 1)];
+  for (int j = 0; j < kMaxTopKPush; j++) {
+    row[j] = inv[t * k + min(j, k - 1)];
+    any |= j < k && row[j] >= r0 && row[j] < r1;
+  }
+  if (!any) return;
   float v[8];
   unpack8(x[(size_t)t * HC + c], v);
   uint2 codes;
@@ -153,7 +174,7 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
   const uint4 hat = pack8(deq);
 #pragma unroll
   for (int j = 0; j < kMaxTopKPush; j++) {
-    if (j < k) {
+    if (j < k && row[j] >= r0 && row[j] < r1) {
       const size_t r = (size_t)row[j];
       xq[r * HC + c] = codes;
       if ((c & 3) == 0) xs[((size_t)(c >> 4) * R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
@@ -162,12 +183,18 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
   }
 }
 
-void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq, uint8_t *xs,
-                             uint16_t *xhat, int T, int k, int H, hipStream_t s) {
+void launch_dispatch_push_mx_range(const uint16_t *x, const int32_t *inv, uint8_t *xq,
+                                   uint8_t *xs, uint16_t *xhat, int T, int k, int H, int r0,
+                                   int r1, hipStream_t s) {
   const long n = (long)T * (H / 8);
   if (n <= 0) return;
   hipLaunchKernelGGL(dispatch_push_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const uint4 *)x, inv, (uint2 *)xq, xs, (uint4 *)xhat, T, k, H / 8);
+                     (const uint4 *)x, inv, (uint2 *)xq, xs, (uint4 *)xhat, T, k, H / 8, r0, r1);
+}
+
+void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq, uint8_t *xs,
+                             uint16_t *xhat, int T, int k, int H, hipStream_t s) {
+  launch_dispatch_push_mx_range(x, inv, xq, xs, xhat, T, k, H, 0, T * k, s);
 }
 
 // Row-wise MX quantisation of a bf16 matrix along its contiguous axis.
