@@ -66,6 +66,9 @@ def _args():
                     help="pipelined schedule: routed rows per minibatch (0 = library default)")
     ap.add_argument("--comm-cus", type=int, default=0,
                     help="pipelined schedule: CUs of the communication stream (0 = share all)")
+    ap.add_argument("--sweep-minibatch", default="",
+                    help="comma-separated minibatch sizes (routed rows): also time the pipelined "
+                         "schedule at each and report forward/backward ms per size")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -207,8 +210,10 @@ def main():
         return evs
 
     def sched_for(evs):
+        """Stage events (None: that boundary is not recorded)."""
         import ctypes
-        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event if e is not None else None
+                                              for e in evs])
         s = m.MoeSched()
         s.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
         s.n_stage_events = len(evs)
@@ -269,6 +274,34 @@ def main():
     pipe_fwd = float(np.mean([f[0].elapsed_time(f[-1]) for f, _ in pev]))
     pipe_bwd = float(np.mean([b[0].elapsed_time(b[-1]) for _, b in pev])) if w.backward else None
 
+    def pipelined_split(mb):
+        """Forward and backward ms of the pipelined schedule at minibatch mb
+        (events at the start and at the join of each direction)."""
+        evs = [(make_events(2), make_events(2)) for _ in range(a.steps)]
+        run = []
+        for f, b in evs:
+            (pf, af), (pb, ab) = sched_for([f[0]] + [None] * 5 + [f[1]]), \
+                sched_for([b[0]] + [None] * 6 + [b[1]])
+            for q in (pf, pb):
+                q.schedule = m.MOE_SCHED_PIPELINED
+                q.minibatch_rows = mb
+                q.comm_cus = a.comm_cus
+            run.append(((pf, af), (pb, ab)))
+        q = pipelined()
+        q.minibatch_rows = mb
+        for _ in range(a.warmup):
+            step(q, q)
+        torch.cuda.synchronize()
+        for (pf, _), (pb, _) in run:
+            step(pf, pb)
+        torch.cuda.synchronize()
+        fwd = float(np.mean([f[0].elapsed_time(f[1]) for f, _ in evs]))
+        bwd = float(np.mean([b[0].elapsed_time(b[1]) for _, b in evs])) if w.backward else None
+        return {"minibatch_rows": mb, "minibatches": -(-w.T * w.k // mb),
+                "layer_fwd_ms": fwd, "layer_bwd_ms": bwd}
+
+    sweep = [pipelined_split(int(v)) for v in a.sweep_minibatch.split(",") if v.strip()]
+
     stage_ms = {}
     for i, name in enumerate(FWD_STAGES):
         stage_ms[name] = float(np.mean([f[i].elapsed_time(f[i + 1]) for f, _ in ev]))
@@ -326,6 +359,8 @@ def main():
                       "minibatch_rows": a.minibatch_rows or "default",
                       "comm_cus": a.comm_cus},
     }
+    if sweep:
+        res["minibatch_sweep"] = sweep
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, min(a.cpu_tokens, w.T))
     print(json.dumps(res), flush=True)

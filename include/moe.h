@@ -117,13 +117,14 @@ enum { MOE_SCHED_STAGED = 0, MOE_SCHED_PERSISTENT = 1, MOE_SCHED_PIPELINED = 2 }
  *             GEMM done, 6 shared expert done, 7 router + reverse-dispatch
  *             done (pipelined: 1-7 at the join). */
 typedef struct moe_sched {
-  int32_t minibatch_rows; /* routed rows per minibatch (0 = default: the
-                             backward takes enough rows for two full waves
-                             of 256 x 256 tiles of its first GEMM (the down
-                             data gradient); the forward takes all rows, the
-                             fastest on one GPU, where a one-minibatch
-                             pipelined forward is the staged one.  Always at
-                             least max(256, ceil(R / 1024))) */
+  int32_t minibatch_rows; /* routed rows per minibatch (0 = default: enough
+                             rows for two full waves of 256 x 256 tiles of
+                             the direction's first GEMM -- gate/up forward,
+                             down data gradient backward -- and in the
+                             forward at least half the rows; always at
+                             least max(256, ceil(R / 1024))).  A
+                             one-minibatch pipelined forward is the staged
+                             forward, on the caller's stream. */
   int32_t ring_slots;     /* minibatches dispatched ahead of the gate/up GEMM
                              (0 = default, 2) */
   int32_t comm_cus;       /* CUs given to dispatch/combine (0 = share all) */

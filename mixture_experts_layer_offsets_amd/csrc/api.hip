@@ -574,24 +574,24 @@ int pipe_resources(int comm_cus, size_t n_events, PipeRes **out) {
   return MOE_OK;
 }
 
-// Rows per minibatch: the caller's, else
-//  - backward: enough rows for two full waves of 256 x 256 tiles of its first
-//    GEMM (the down data gradient, I columns) [KC §02: a minibatch should fill
-//    the compute units at least twice];
-//  - forward (fwd = true): all rows.  Measured on MI355X at the Kimi-shaped
-//    share: with two minibatches the forward is ~0.1 ms slower than one
-//    pass -- on one GPU dispatch and combine are HBM copies of ~50 us each,
-//    there is little to hide, and every cross-stream hand-off adds latency;
-//    the backward gains from running its weight gradients beside the data
-//    gradients.
-// Never below the plan's bound.
+// Rows per minibatch: the caller's, else enough rows for two full waves of
+// 256 x 256 tiles of the direction's first GEMM [KC §02: a minibatch should
+// fill the compute units at least twice] -- the forward's gate/up GEMM (2I
+// columns) or the backward's down data gradient (I columns) -- and, in the
+// forward, at least half the rows.  Measured on MI355X: at the Kimi-shaped
+// share two forward minibatches beat one (the second's dispatch and the
+// first's GEMM tail overlap), but at the DeepSeek-V3 shape (256 experts)
+// every further minibatch costs more -- each adds a partly filled row tile
+// per expert it cuts and a few cross-stream hand-offs, while on one GPU the
+// exchange it would hide is only an HBM copy.  Never below the plan's bound.
 long pipe_minibatch(const Dims &d, const moe_sched *sc, bool fwd) {
   long mb = sc->minibatch_rows;
   if (mb <= 0) {
-    if (fwd) return d.R;
-    const long n_tiles = (d.I + kTileN - 1) / kTileN;
+    const long n_cols = fwd ? 2 * d.I : d.I;
+    const long n_tiles = (n_cols + kTileN - 1) / kTileN;
     const long row_tiles = (2L * std::max(device_cus(), 1) + n_tiles - 1) / n_tiles;
     mb = row_tiles * kTileM;
+    if (fwd) mb = std::max(mb, (d.R + 1) / 2);
   }
   return std::min(std::max(mb, mk_min_minibatch(d)), d.R);
 }
@@ -630,13 +630,16 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k, R = (int)d.R;
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes *r = nullptr;
-  int rc = pipe_resources(sc->comm_cus, 3 * (size_t)NM + 4, &r);
+  int rc = pipe_resources(sc->comm_cus, 3 * (size_t)NM + 5, &r);
   if (rc) return rc;
-  const int evD = 0, evG1 = NM, evG2 = 2 * NM, evX = 3 * NM;
+  const int evD = 0, evG1 = NM, evG2 = 2 * NM, evX = 3 * NM, evPlan = 3 * NM + 4;
   const PipeCtx c{r, s};
-  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
-                   w.tlf_off, w.tlb, w.tlb_off, s);
   if (!c.fork(evX)) return MOE_ERR_HIP;
+  // the plan (GEMM offsets, token lists) runs beside the first dispatch,
+  // which needs only inv
+  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
+                   w.tlf_off, w.tlb, w.tlb_off, r->gemm[0]);
+  if (!c.rec(r->gemm[0], evPlan) || !c.wait(r->gemm[1], evPlan)) return MOE_ERR_HIP;
   if (d.shared) {
     hipStream_t q = r->gemm[0];
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, q);
@@ -668,6 +671,8 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
     return c.rec(q, evG2 + m);
   };
   auto C = [&](int m) {
+    // down(m) follows the plan on its stream, so waiting for it covers the
+    // token lists too
     if (!c.wait(r->comm, evG2 + m) || (m > 0 && !c.wait(r->comm, evG2 + m - 1))) return false;
     launch_combine_list(sv.y, sv.w, sv.inv, d.shared ? sv.y_s : nullptr, out, w.tlf, w.tlf_off, m,
                         T, k, H, r->comm);
@@ -713,10 +718,13 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   const int evRC = 0, evDG = NM, evX = 2 * NM;
   const PipeCtx c{r, s};
   const bool router = w_router != nullptr;
-  if (router) launch_transpose_pack(w_router, w.wrT, 1, H, E, E, 32, 0, s);
-  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
-                   w.tlf_off, w.tlb, w.tlb_off, s);
   if (!c.fork(evX)) return MOE_ERR_HIP;
+  // the plan (and the router's W_r^T) run on GEMM stream 0 beside the first
+  // reverse-combine, which needs neither; the communication stream waits for
+  // them before its first reverse-dispatch
+  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
+                   w.tlf_off, w.tlb, w.tlb_off, r->gemm[0]);
+  if (router) launch_transpose_pack(w_router, w.wrT, 1, H, E, E, 32, 0, r->gemm[0]);
   if (d.shared) {
     hipStream_t q = r->gemm[0];
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, q);
@@ -744,6 +752,7 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
     return c.rec(q, evDG + m);
   };
   auto RD = [&](int m) {
+    // DG(m) follows the plan and W_r^T on GEMM stream 0
     if (!c.wait(r->comm, evDG + m)) return false;
     launch_reverse_dispatch_list(w.dX, sv.inv, sv.idx, sv.w, dw, w.dsel,
                                  router ? w.wrT : nullptr, d.shared ? w.dxs : nullptr, dx, w.tlb,
