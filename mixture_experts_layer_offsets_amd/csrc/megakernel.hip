@@ -156,7 +156,9 @@ __device__ void dispatch_rows(const MkArgs &a, int r0, int r1) {
       uint2 codes;
       const uint32_t sc = mx_quad8(f, &codes, deq);
       ((uint2 *)a.xq)[(size_t)r * HC + c] = codes;
-      if ((c & 3) == 0) a.xs[(size_t)r * (HC / 4) + c / 4] = (uint8_t)sc;
+      // scales K-blocked, as every consumer reads them: block b = c/4 of
+      // row r at byte (b/4 * R + r) * 4 + b%4
+      if ((c & 3) == 0) a.xs[((size_t)(c >> 4) * a.R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
       ((uint4 *)a.x_perm)[(size_t)r * HC + c] = pack8(deq);
     }
   }
