@@ -69,6 +69,9 @@ def _args():
     ap.add_argument("--sweep-minibatch", default="",
                     help="comma-separated minibatch sizes (routed rows): also time the pipelined "
                          "schedule at each and report forward/backward ms per size")
+    ap.add_argument("--decode-tokens", type=int, default=0,
+                    help="also time the few-token inference forward (moe_decode_fwd) on the first "
+                         "N tokens of the workload, against moe_layer_fwd on the same tokens")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -302,6 +305,43 @@ def main():
 
     sweep = [pipelined_split(int(v)) for v in a.sweep_minibatch.split(",") if v.strip()]
 
+    def decode_bench(n):
+        """moe_decode_fwd on the first n tokens (same weights and routing),
+        HIP events on the current stream around K calls; bytes = the weights
+        of the experts those tokens select (+ the shared expert), read once."""
+        sh = m.Shape(n, w.H, w.E, w.k, w.I, w.shared_I, m.MOE_BF16)
+        L = m.MoeLayer(sh, dev)
+        L.prepare(d(inp["w_gate"]), d(inp["w_up"]), d(inp["w_down"]), d(inp["ws_gate"]),
+                  d(inp["ws_up"]), d(inp["ws_down"]))
+        kw = dict(w_router=wr, bias=bias)
+        if wr is None:
+            kw = dict(topk_idx=idx[:n].contiguous(), topk_w=tw[:n].contiguous())
+        xs = x[:n].contiguous()
+
+        def timed(fn):
+            for _ in range(a.warmup):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(a.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / a.steps
+
+        t_dec = timed(lambda: L.decode(xs, **kw))
+        t_fwd = timed(lambda: L.forward(xs, **kw))
+        if wr is None:
+            used = len(np.unique(inp["topk_idx"][:n]))
+        else:
+            used = len(np.unique(L.saved_tensor("topk_idx", torch.int32, (n, w.k)).cpu().numpy()))
+        wbytes = (used * 3 * w.H * w.I + 3 * w.H * w.shared_I) * 2
+        gbs = wbytes / (t_dec * 1e-3) / 1e9
+        return {"tokens": n, "decode_ms": t_dec, "layer_fwd_ms": t_fwd, "experts_read": used,
+                "weight_bytes": wbytes, "achieved_GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+
+    decode = decode_bench(a.decode_tokens) if a.decode_tokens > 0 and not w.mx else None
+
     stage_ms = {}
     for i, name in enumerate(FWD_STAGES):
         stage_ms[name] = float(np.mean([f[i].elapsed_time(f[i + 1]) for f, _ in ev]))
@@ -361,6 +401,8 @@ def main():
     }
     if sweep:
         res["minibatch_sweep"] = sweep
+    if decode:
+        res["decode"] = decode
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, min(a.cpu_tokens, w.T))
     print(json.dumps(res), flush=True)

@@ -261,6 +261,27 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched,
                   float *dw_gate, float *dw_up, float *dw_down, float *dws,
                   float *dtopk_w, void *ws, size_t ws_bytes, void *stream);
 
+/* Few-token inference forward (decode): the same layer output as
+ * moe_layer_fwd -- routing, layout, expert FFN, shared expert, combine --
+ * for a small token count, with no forward context and no backward.  The
+ * pages mention a separate decode kernel for inference in which each token
+ * gets its own small group of threads [NA design].  With few tokens the
+ * layer is bound by reading the selected experts' weights, so the expert FFN
+ * here streams each used expert's packed weight rows once, in 16-byte
+ * chunks across a wave, and applies them to all of that expert's routed
+ * rows (8 per pass; an expert with more rows re-reads its weights per 8),
+ * with fp32 accumulation and a fixed-order lane sum (deterministic).  Meant
+ * for T*k up to a few hundred rows; larger batches belong to
+ * moe_layer_fwd's MFMA grouped GEMMs.  Arguments as moe_layer_fwd (x [T][H]
+ * bf16; router w_router/bias or supplied topk_idx/topk_w; packed from
+ * moe_prepare_weights; out [T][H] bf16; ws of moe_workspace_bytes).  bf16
+ * only: MXFP8 shapes return MOE_ERR_UNSUPPORTED. */
+int moe_decode_fwd(const moe_shape *shape, const uint16_t *x,
+                   const uint16_t *w_router, const float *bias,
+                   const int32_t *topk_idx_in, const float *topk_w_in,
+                   const void *packed, uint16_t *out, void *ws,
+                   size_t ws_bytes, void *stream);
+
 /* Device pointers into a forward context (host call, no device work):
  * where moe_layer_fwd left each intermediate.  Any field may be NULL in
  * the result when the shape has no such tensor. */

@@ -65,6 +65,7 @@ SIGNATURES = {
     "moe_combine": (c_int, [c_void_p] * 6 + [c_void_p]),
     "moe_layer_fwd": (c_int, [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p]),
     "moe_layer_bwd": (c_int, [c_void_p] * 14 + [c_void_p, c_size_t, c_void_p]),
+    "moe_decode_fwd": (c_int, [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]),
     "moe_saved_pointers": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_read_status": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_strerror": (ctypes.c_char_p, [c_int]),
@@ -209,6 +210,13 @@ def moe_layer_bwd(shape, sched, dout, x, w_router, saved, packed, dx, dw_router,
                              _p(saved), _p(packed), _p(dx), _p(dw_router), _p(dw_gate),
                              _p(dw_up), _p(dw_down), _p(dws), _p(dtopk_w), _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_bwd")
+
+
+def moe_decode_fwd(shape, x, w_router, bias, topk_idx_in, topk_w_in, packed, out, ws,
+                   stream=None):
+    _ck(load().moe_decode_fwd(_shape(shape), _p(x), _p(w_router), _p(bias), _p(topk_idx_in),
+                              _p(topk_w_in), _p(packed), _p(out), _p(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_decode_fwd")
 
 
 def moe_saved_pointers(shape, saved) -> dict:

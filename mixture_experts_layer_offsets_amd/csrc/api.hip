@@ -148,6 +148,9 @@ struct Work {
   // pipelined schedule: per-minibatch group offsets and tile prefixes, and
   // the token lists of the forward combine and the backward reverse-dispatch
   int32_t *pm_off, *pm_ts, *tlf, *tlf_off, *tlb, *tlb_off;
+  // decode forward: its routing and layout (it has no forward context)
+  int32_t *dec_idx, *dec_counts, *dec_offsets, *dec_perm, *dec_inv;
+  float *dec_w, *dec_logits;
 };
 
 // Smallest minibatch the persistent forward accepts, and its count bound.
@@ -183,6 +186,13 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   t.tlf_off = c.take<int32_t>(t.max_nm + 1);
   t.tlb = c.take<int32_t>(d.T);
   t.tlb_off = c.take<int32_t>(t.max_nm + 1);
+  t.dec_idx = c.take<int32_t>(d.R);
+  t.dec_w = c.take<float>(d.R);
+  t.dec_logits = c.take<float>(d.T * d.E);
+  t.dec_counts = c.take<int32_t>(d.E);
+  t.dec_offsets = c.take<int32_t>(d.E + 1);
+  t.dec_perm = c.take<int32_t>(d.R);
+  t.dec_inv = c.take<int32_t>(d.R);
   const size_t union_start = c.off;
   // forward-only pieces (standalone expert FFN)
   t.act = c.take<uint16_t>(d.R * d.I);
@@ -1097,6 +1107,60 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   launch_reverse_dispatch(w.dX, sv.inv, sv.idx, router ? w.dsel : nullptr,
                           router ? w.wrT : nullptr, d.shared ? w.dxs : nullptr, dx, T, k, H, s);
   st.mark(7);
+  return hip_status();
+}
+
+int moe_decode_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_router,
+                   const float *bias, const int32_t *topk_idx_in, const float *topk_w_in,
+                   const void *packed, uint16_t *out, void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (d.mx) return MOE_ERR_UNSUPPORTED;
+  if (!x || !packed || !out || !ws) return MOE_ERR_INVALID_ARG;
+  const bool router = w_router != nullptr;
+  if (router == (topk_idx_in != nullptr) || (topk_idx_in != nullptr) != (topk_w_in != nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (router && (d.k > d.E)) return MOE_ERR_INVALID_ARG;
+  if (router && d.E % 8) return MOE_ERR_UNSUPPORTED;
+  Work w;
+  if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  Packed p;
+  carve_packed(d, packed, &p);
+  hipStream_t s = S(stream);
+  const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k;
+  launch_fill_i32(w.status, 1, MOE_OK, s);
+  // routing: from the router, or the caller's supplied arrays read in place
+  const int32_t *idx = topk_idx_in;
+  const float *wts = topk_w_in;
+  if (router) {
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
+    GemmArgs lg{};
+    lg.A = x; lg.lda = H;
+    lg.B = w_router; lg.ldb = E;
+    lg.C = w.dec_logits; lg.ldc = E;
+    lg.bias = bias;
+    lg.offsets = w.dense_offsets; lg.tile_start = w.dense_tiles;
+    lg.G = 1; lg.N = E; lg.K = H;
+    launch_gemm_rows(lg, EPI_F32, false, T, s);
+    launch_topk(w.dec_logits, T, E, k, w.dec_idx, w.dec_w, s);
+    idx = w.dec_idx;
+    wts = w.dec_w;
+  }
+  if (d.R <= kDecLayoutMax)
+    launch_decode_layout(idx, (int)d.R, E, w.dec_counts, w.dec_offsets, w.dec_perm, w.dec_inv, s);
+  else
+    launch_layout(idx, (int)d.R, E, w.chunk_counts, w.dec_counts, w.dec_offsets, w.dec_perm,
+                  w.dec_inv, w.tile_start, kTileM, w.order, s);
+  // routed experts: rows grouped by expert, x gathered through perm
+  launch_decode_ffn(x, w.dec_perm, w.dec_offsets, E, k, H, (int)d.I, p.r.guT, p.r.dT, w.act,
+                    w.dX, s);
+  if (d.shared) {
+    launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
+    launch_decode_ffn(x, nullptr, w.dense_offsets, 1, 1, H, (int)d.Is, p.s.guT, p.s.dT, w.dh_s,
+                      w.dxs, s);
+  }
+  launch_combine(w.dX, wts, w.dec_inv, d.shared ? w.dxs : nullptr, out, T, k, H, s);
   return hip_status();
 }
 

@@ -81,6 +81,19 @@ void launch_reverse_dispatch_list(const uint16_t *dX, const int32_t *inv, const 
                                   const int32_t *tl, const int32_t *tl_off, int m, int T, int k,
                                   int H, hipStream_t s);
 
+// decode.hip: few-token expert FFN (weight-streaming GEMV form).  For each of
+// G groups (experts; offsets [G+1]) and its rows r: act[r] = silu(x[t] Wg) *
+// (x[t] Wu), y[r] = act[r] Wd, t = perm[r] / k (perm == nullptr: t = r).
+// guT: packed gate/up [G][2I][H]; dT: packed down [G][H][I].
+void launch_decode_ffn(const uint16_t *x, const int32_t *perm, const int32_t *offsets, int G,
+                       int k, int H, int I, const uint16_t *guT, const uint16_t *dT,
+                       uint16_t *act, uint16_t *y, hipStream_t s);
+// The layer's layout (counts, offsets, perm, inv; same result as
+// launch_layout) in one workgroup, for R <= kDecLayoutMax routed rows.
+constexpr int kDecLayoutMax = 1024;
+void launch_decode_layout(const int32_t *idx, int R, int E, int32_t *counts, int32_t *offsets,
+                          int32_t *perm, int32_t *inv, hipStream_t s);
+
 // gemm.hip: grouped GEMMs on MFMA (bf16 inputs, fp32 accumulation)
 enum EpiKind { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_WGRAD_GU = 4 };
 

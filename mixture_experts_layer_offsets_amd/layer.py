@@ -40,6 +40,14 @@ class MoeLayer:
                            self.saved, self.ws)
         return out
 
+    def decode(self, x, w_router=None, bias=None, topk_idx=None, topk_w=None, out=None):
+        """Few-token inference forward (no forward context is written)."""
+        s = self.shape
+        if out is None:
+            out = torch.empty((s.tokens, s.hidden), dtype=torch.int16, device=self.device)
+        _lib.moe_decode_fwd(s, x, w_router, bias, topk_idx, topk_w, self.packed, out, self.ws)
+        return out
+
     def backward(self, dout, x, w_router=None, sched=None, grads=None):
         s = self.shape
         dev = self.device
