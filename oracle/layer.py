@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mx import mx_quantize, mx_roundtrip
+from .mx import mx_quantize, mx_roundtrip, mx_rows_roundtrip
 from .numerics import bf16, bf16_bits, bf16_to_f64, f32, identity
 
 
@@ -256,7 +256,7 @@ def combine(Y, w, inv, k, y_shared=None, exact=False):
     return R.bf16(acc)
 
 
-def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R):
+def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R, mx_wgrad=False):
     """Backward of one expert's SwiGLU FFN given its rows' output gradient dY.
 
     dA = dY' Wd^T; dg = dA u silu'(g); du = dA silu(g) (stored as bf16);
@@ -264,30 +264,40 @@ def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R):
     dX = dg' Wg^T + du' Wu^T (bf16).  With MXFP8 the data-gradient GEMM
     operands dY' and dg', du' are the MX round trips of the stored bf16
     tensors (along H and along I); the weight-gradient GEMMs use the bf16
-    tensors.  silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
+    tensors -- or, with mx_wgrad, MX round trips of them quantised along the
+    rows, i.e. along those GEMMs' contraction axis, in 32-row blocks starting
+    at the expert's first row (the last block zero-padded).
+    silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
     """
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
     dA = R.f32(dYq @ Wb["d_b"].T)
     s = sigmoid(g)
     dg = R.bf16(dA * u * s * (1.0 + g * (1.0 - s)))
     du = R.bf16(dA * g * s)
-    dWd = R.f32(ahat.T @ dY)
-    dWg = R.f32(Xhat.T @ dg)
-    dWu = R.f32(Xhat.T @ du)
+    if mx and mx_wgrad:
+        aw, dYw = mx_rows_roundtrip(ahat), mx_rows_roundtrip(dY)
+        Xw, dgw, duw = mx_rows_roundtrip(Xhat), mx_rows_roundtrip(dg), mx_rows_roundtrip(du)
+    else:
+        aw, dYw, Xw, dgw, duw = ahat, dY, Xhat, dg, du
+    dWd = R.f32(aw.T @ dYw)
+    dWg = R.f32(Xw.T @ dgw)
+    dWu = R.f32(Xw.T @ duw)
     dgq = mx_roundtrip(dg, axis=1) if mx else dg
     duq = mx_roundtrip(du, axis=1) if mx else du
     dX = R.bf16(dgq @ Wb["g_b"].T + duq @ Wb["u_b"].T)
     return dict(dA=dA, dg=dg, du=du, dWd=dWd, dWg=dWg, dWu=dWu, dX=dX)
 
 
-def backward(inp, fw, dout=None):
+def backward(inp, fw, dout=None, mx_wgrad=False):
     """The layer's backward pass, mirroring the forward's data movement.
 
     Training adds two more exchange rounds in the opposite direction [KC §01]:
     reverse-combine (each sorted row pulls its token's output gradient times
     the slot weight) and reverse-dispatch (each token sums the gradients of
     its k rows) [KC §02].  Returns dY, dw, per-expert dg/du, dX, dW_gate,
-    dW_up, dW_down, the router's dL/dW_r (router routing) and dx.
+    dW_up, dW_down, the router's dL/dW_r (router routing) and dx.  With
+    MXFP8 and mx_wgrad the weight-gradient GEMMs also take MX operands
+    (see _swiglu_rows_bwd); the shared expert's too.
     """
     k, mx, exact = fw["k"], fw["mx"], fw["exact"]
     R = _Round(exact)
@@ -315,7 +325,7 @@ def backward(inp, fw, dout=None):
             continue
         Wb = dict(d_b=W["d_b"][e], g_b=W["g_b"][e], u_b=W["u_b"][e])
         b = _swiglu_rows_bwd(fw["Xhat"][rs], fw["g"][rs], fw["u"][rs], fw["ahat"][rs],
-                             dY[rs], Wb, mx, R)
+                             dY[rs], Wb, mx, R, mx_wgrad)
         dg[rs], du[rs], dX[rs] = b["dg"], b["du"], b["dX"]
         dWg[e], dWu[e], dWd[e] = b["dWg"], b["dWu"], b["dWd"]
     out = dict(dY=dY, dw=dw, dg=dg, du=du, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd)
@@ -331,7 +341,7 @@ def backward(inp, fw, dout=None):
         sh = fw["shared"]
         WS = fw["WS"]
         b = _swiglu_rows_bwd(fw["xhat_tok"], sh["g"], sh["u"], sh["ahat"], dout,
-                             dict(d_b=WS["d_b"], g_b=WS["g_b"], u_b=WS["u_b"]), mx, R)
+                             dict(d_b=WS["d_b"], g_b=WS["g_b"], u_b=WS["u_b"]), mx, R, mx_wgrad)
         out.update(dWsg=b["dWg"], dWsu=b["dWu"], dWsd=b["dWd"], dXs=b["dX"])
         acc += b["dX"]
     out["dx"] = R.bf16(acc)

@@ -105,3 +105,17 @@ def mx_roundtrip(v, axis: int = -1) -> np.ndarray:
     """deq(MXQ(v)): the value a consumer of the quantised tensor sees."""
     c, s = mx_quantize(v, axis)
     return mx_dequantize(c, s, axis)
+
+
+def mx_rows_roundtrip(v) -> np.ndarray:
+    """deq(MXQ(v)) with the 32-value blocks running down the rows (axis 0) of
+    a 2-D tensor: rows 32b .. 32b+31 of each column share one scale.  A row
+    count that is not a multiple of 32 is zero-padded for the quantisation
+    (zeros change no block maximum and quantise to zero); the pad is dropped.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    pad = (-n) % BLOCK
+    if pad:
+        v = np.concatenate([v, np.zeros((pad,) + v.shape[1:])], axis=0)
+    return mx_roundtrip(v, axis=0)[:n]

@@ -122,3 +122,95 @@ def test_zero_block():
 def test_non_multiple_of_32_rejected():
     with pytest.raises(ValueError):
         mx_quantize(np.zeros((1, 48)), axis=1)
+
+
+# --- quantisation down the rows (the MX weight-gradient recipe) -------------
+
+def _representable_rows(n, m, seed):
+    """An n x m matrix whose 32-row blocks (per column) are exactly
+    representable: each block gets its own scale 2^s, one element of E4M3
+    exponent 8 (so the block maximum selects exactly s) and the rest E4M3
+    values that include subnormals (which a wrong block grouping, choosing a
+    larger scale, would round away)."""
+    rng = np.random.default_rng(seed)
+    v = np.zeros((n, m))
+    top = 256.0 + 32.0 * np.arange(7)          # E4M3 values with exponent 8: 256 .. 448
+    small = np.ldexp(np.arange(1, 8), -9)       # E4M3 subnormals
+    mid = np.ldexp(8.0 + np.arange(8), -3)      # normals in [1, 2)
+    for b0 in range(0, n, 32):
+        rows = min(32, n - b0)
+        for c in range(m):
+            s = int(rng.integers(-20, 20))
+            blk = rng.choice(np.concatenate([small, mid, -small, -mid]), rows)
+            blk[rng.integers(rows)] = rng.choice(top) * rng.choice([-1.0, 1.0])
+            v[b0:b0 + rows, c] = np.ldexp(blk, s)
+    return v
+
+
+def test_rows_roundtrip_identity_on_representable_blocks():
+    from oracle.mx import mx_roundtrip, mx_rows_roundtrip
+    v = _representable_rows(96, 32, seed=1)
+    assert np.array_equal(mx_rows_roundtrip(v), v)
+    # quantising along the other axis instead loses the per-row-block scales
+    assert not np.array_equal(mx_roundtrip(v, axis=1), v)
+
+
+def test_rows_roundtrip_ragged_segment_zero_padded():
+    from oracle.mx import mx_rows_roundtrip
+    v = _representable_rows(37, 4, seed=2)      # last block holds 5 real rows
+    assert np.array_equal(mx_rows_roundtrip(v), v)
+    r = np.random.default_rng(3).standard_normal((37, 6))
+    padded = np.vstack([r, np.zeros((27, 6))])
+    assert np.array_equal(mx_rows_roundtrip(r), mx_rows_roundtrip(padded)[:37])
+
+
+def test_rows_roundtrip_matches_column_quantiser_transposed():
+    from oracle.mx import mx_roundtrip, mx_rows_roundtrip
+    r = np.random.default_rng(4).standard_normal((64, 7)) * 3.0
+    # blocks down the rows of r are blocks along the columns of r^T
+    assert np.array_equal(mx_rows_roundtrip(r), mx_roundtrip(r.T, axis=1).T)
+    assert not np.array_equal(mx_rows_roundtrip(r[:, :32 * 0 + 7]), r)
+
+
+def test_rows_roundtrip_product_within_e4m3_bound():
+    """|Q(A)^T Q(B) - A^T B| within the bound E4M3/E8M0 rounding allows:
+    per value |q - v| <= 2^-4 |v| + 2^-18 amax(block) + max(0, |v| - 448 2^s)
+    with 2^s = 2^(floor(log2 amax) - 8): half an ulp with 3 mantissa bits;
+    below the normals half the 2^-9 quantum of 2^s (2^s <= amax / 256); and
+    the saturation of block values between 448 and 512 times 2^s."""
+    from oracle.mx import mx_rows_roundtrip
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((70, 9)) * np.exp(rng.standard_normal((70, 1)))
+    B = rng.standard_normal((70, 11))
+
+    def err_bound(M):
+        pad = np.vstack([np.abs(M), np.zeros(((-len(M)) % 32, M.shape[1]))])
+        amax = pad.reshape(-1, 32, M.shape[1]).max(axis=1)
+        amax_rows = np.repeat(amax, 32, axis=0)[:len(M)]
+        scale = np.ldexp(1.0, np.frexp(amax_rows)[1] - 1 - 8)
+        return (2.0 ** -4 * np.abs(M) + 2.0 ** -18 * amax_rows
+                + np.maximum(0.0, np.abs(M) - 448.0 * scale))
+
+    eA, eB = err_bound(A), err_bound(B)
+    qA, qB = mx_rows_roundtrip(A), mx_rows_roundtrip(B)
+    assert np.all(np.abs(qA - A) <= eA) and np.all(np.abs(qB - B) <= eB)
+    bound = eA.T @ np.abs(B) + np.abs(A).T @ eB + eA.T @ eB
+    assert np.all(np.abs(qA.T @ qB - A.T @ B) <= bound * (1 + 1e-12))
+    # and the quantisation is not the identity on these inputs
+    assert np.abs(qA - A).max() > 0
+
+
+def test_backward_mx_wgrad_recipe():
+    """With MXFP8 and mx_wgrad the weight gradients move by at most the MX
+    error of their operands; the data gradients do not move at all."""
+    import oracle
+    import synth
+    w = synth.custom(T=48, H=128, E=3, k=2, I=64, routing="supplied", mx=True, seed=9)
+    inp = synth.make_inputs(w)
+    fw = oracle.forward(inp, w.k, mx=True)
+    b0 = oracle.backward(inp, fw)
+    b1 = oracle.backward(inp, fw, mx_wgrad=True)
+    assert np.array_equal(b0["dx"], b1["dx"]) and np.array_equal(b0["dX"], b1["dX"])
+    for key in ("dWg", "dWu", "dWd"):
+        d = np.abs(b1[key] - b0[key]).max() / np.abs(b0[key]).max()
+        assert 0 < d < 0.1, (key, d)
