@@ -72,6 +72,8 @@ def _args():
     ap.add_argument("--decode-tokens", type=int, default=0,
                     help="also time the few-token inference forward (moe_decode_fwd) on the first "
                          "N tokens of the workload, against moe_layer_fwd on the same tokens")
+    ap.add_argument("--mx-wgrad", action="store_true",
+                    help="MXFP8 workloads: weight-gradient GEMMs on MX operands too")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -223,6 +225,10 @@ def main():
         return s, arr
 
     def step(sf=None, sb=None):
+        if a.mx_wgrad and w.mx:
+            if sb is None:
+                sb = m.MoeSched()
+            sb.mx_wgrad = 1
         layer.forward(x, w_router=wr, bias=bias, topk_idx=idx, topk_w=tw, out=out, sched=sf)
         if w.backward:
             layer.backward(dout, x, w_router=wr, grads=grads, sched=sb)
@@ -351,7 +357,8 @@ def main():
     flops, byts = _algorithmic(w)
 
     def peak(stage):
-        return PEAK_FP8_TFLOPS if w.mx and stage in MX_GEMMS else PEAK_BF16_TFLOPS
+        mx_stage = stage in MX_GEMMS or (a.mx_wgrad and stage.startswith("gemm_wgrad"))
+        return PEAK_FP8_TFLOPS if w.mx and mx_stage else PEAK_BF16_TFLOPS
     mfma = {k: flops[k] / (stage_ms[k] * 1e-3) / 1e12 / peak(k)
             for k in flops if k in stage_ms and stage_ms[k] > 0}
     hbm = {k: byts[k] / (stage_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS
@@ -374,7 +381,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if w.mx else "bf16",
+        "dtype": ("mxfp8 (weight gradients too)" if a.mx_wgrad else "mxfp8") if w.mx else "bf16",
         "data": "synthetic (seeded; random-init weights; supplied Zipf routing)"
                 if w.routing == "supplied" else "synthetic (seeded; random-init weights)",
         "config": {"workload": f"{w.name}: T={w.T} tokens, top-{w.k} ({w.T * w.k} routed rows), "

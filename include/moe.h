@@ -133,6 +133,12 @@ typedef struct moe_sched {
   int32_t n_stage_events;
   int32_t watchdog_us;    /* persistent kernel only: microseconds one wait may
                              take before it gives up (0 = default, 2 s) */
+  int32_t mx_wgrad;       /* MXFP8 shapes: 1 = the weight-gradient GEMMs also
+                             take MX operands, quantised down the rows (the
+                             GEMMs' contraction axis) in E8M0 blocks of 32
+                             rows starting at each expert's first row, the
+                             last block zero-padded; 0 (default) = bf16
+                             weight gradients on the MX round trips */
 } moe_sched;
 
 /* ------------------------------------------------------------------ sizes */
@@ -306,6 +312,18 @@ typedef struct moe_saved_view {
 
 int moe_saved_pointers(const moe_shape *shape, void *saved,
                        moe_saved_view *view);
+
+/* Device pointers into a workspace (host call, no device work): where the
+ * last moe_layer_bwd that used `ws` left its row intermediates, for callers
+ * that inspect them (valid until the next call that uses `ws`).  Fields
+ * are NULL when the shape is invalid. */
+typedef struct moe_work_view {
+  uint16_t *dy;       /* bf16 [R][H]: rows' output gradient (reverse-combine) */
+  uint16_t *dh;       /* bf16 [R][2I]: dg and du, interleaved in 32-column blocks */
+  uint16_t *dx_rows;  /* bf16 [R][H]: rows' input gradient (before reverse-dispatch) */
+} moe_work_view;
+
+int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view);
 
 /* Reads the device status word of the last layer call that used `ws`
  * (synchronises `stream`).  *status_host = MOE_OK or MOE_ERR_DEVICE_TIMEOUT. */

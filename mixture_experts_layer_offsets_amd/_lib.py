@@ -42,7 +42,7 @@ class MoeSched(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
                 ("comm_cus", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(c_void_p)), ("n_stage_events", ctypes.c_int32),
-                ("watchdog_us", ctypes.c_int32)]
+                ("watchdog_us", ctypes.c_int32), ("mx_wgrad", ctypes.c_int32)]
 
 
 class MoeSavedView(ctypes.Structure):
@@ -67,6 +67,7 @@ SIGNATURES = {
     "moe_layer_bwd": (c_int, [c_void_p] * 14 + [c_void_p, c_size_t, c_void_p]),
     "moe_decode_fwd": (c_int, [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]),
     "moe_saved_pointers": (c_int, [c_void_p, c_void_p, c_void_p]),
+    "moe_workspace_pointers": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_read_status": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_strerror": (ctypes.c_char_p, [c_int]),
 }
@@ -224,6 +225,17 @@ def moe_saved_pointers(shape, saved) -> dict:
     _ck(load().moe_saved_pointers(_shape(shape), _p(saved), ctypes.byref(view)),
         "moe_saved_pointers")
     return {n: getattr(view, n) for n, _ in MoeSavedView._fields_}
+
+
+class MoeWorkView(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("dy", "dh", "dx_rows")]
+
+
+def moe_workspace_pointers(shape, ws) -> dict:
+    view = MoeWorkView()
+    _ck(load().moe_workspace_pointers(_shape(shape), _p(ws), ctypes.byref(view)),
+        "moe_workspace_pointers")
+    return {n: getattr(view, n) for n, _ in MoeWorkView._fields_}
 
 
 def moe_read_status(ws, stream=None) -> int:

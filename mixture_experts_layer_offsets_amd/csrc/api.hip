@@ -148,6 +148,12 @@ struct Work {
   // pipelined schedule: per-minibatch group offsets and tile prefixes, and
   // the token lists of the forward combine and the backward reverse-dispatch
   int32_t *pm_off, *pm_ts, *tlf, *tlf_off, *tlb, *tlb_off;
+  // MX weight gradients: padded expert offsets and the transposed MX
+  // operands (routed; the shared expert's own, since the pipelined backward
+  // runs it beside the routed weight gradients)
+  int32_t *poff, *poff_s;
+  long Rp, Rp_s;
+  MxT wq_a, wq_b, wq_as, wq_bs;
   // decode forward: its routing and layout (it has no forward context)
   int32_t *dec_idx, *dec_counts, *dec_offsets, *dec_perm, *dec_inv;
   float *dec_w, *dec_logits;
@@ -186,6 +192,8 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   t.tlf_off = c.take<int32_t>(t.max_nm + 1);
   t.tlb = c.take<int32_t>(d.T);
   t.tlb_off = c.take<int32_t>(t.max_nm + 1);
+  t.poff = c.take<int32_t>(d.E + 1);
+  t.poff_s = c.take<int32_t>(2);
   t.dec_idx = c.take<int32_t>(d.R);
   t.dec_w = c.take<float>(d.R);
   t.dec_logits = c.take<float>(d.T * d.E);
@@ -210,6 +218,10 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   if (d.mx) {
     t.dyq = take_mx(c, d.R, d.H);
     t.dhq = take_mx(c, d.R, 2 * d.I);
+    // every expert segment padded to 128 rows: at most R + 127 E rows
+    t.Rp = (d.R + 127 * d.E + 127) / 128 * 128;
+    t.wq_a = take_mx(c, t.Rp, std::max(d.H, d.I));
+    t.wq_b = take_mx(c, t.Rp, std::max(d.H, 2 * d.I));
   }
   if (d.shared) {
     t.dh_s = c.take<uint16_t>(d.T * 2 * d.Is);
@@ -217,6 +229,9 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
     if (d.mx) {
       t.doutq = take_mx(c, d.T, d.H);
       t.dhq_s = take_mx(c, d.T, 2 * d.Is);
+      t.Rp_s = (d.T + 127) / 128 * 128;
+      t.wq_as = take_mx(c, t.Rp_s, std::max(d.H, d.Is));
+      t.wq_bs = take_mx(c, t.Rp_s, std::max(d.H, 2 * d.Is));
     }
   }
   if (c.off < fwd_end) c.off = fwd_end;
@@ -412,22 +427,75 @@ void gemm_wgrad_gate_up(const uint16_t *X, const uint16_t *dh, const int32_t *of
   launch_gemm_wgrad(e, EPI_WGRAD_GU, s);
 }
 
+// MX weight gradients: both operands quantised down the rows per expert
+// segment (poff: the segments padded to 128 rows; Rp: the row stride of the
+// transposed codes), then the per-expert MX GEMM.
+struct MxWgrad {
+  const int32_t *poff;
+  long Rp;
+  MxT a, b;
+};
+
+void gemm_wgrad_down_mx(const uint16_t *act, const uint16_t *dY, const int32_t *offsets,
+                        const int32_t *order, int G, long H, long I, float *dWd,
+                        const MxWgrad &m, hipStream_t s) {
+  launch_quant_cols_mx(act, 0, (int)I, offsets, m.poff, G, m.Rp, m.a.q, m.a.s, s);
+  launch_quant_cols_mx(dY, 0, (int)H, offsets, m.poff, G, m.Rp, m.b.q, m.b.s, s);
+  GemmArgs b{};
+  b.A = (const uint16_t *)m.a.q; b.lda = m.Rp;
+  b.B = (const uint16_t *)m.b.q; b.ldb = m.Rp;
+  b.C = dWd; b.ldc = H; b.sC = I * H;
+  b.offsets = m.poff; b.order = order;
+  b.G = G; b.M = (int)I; b.N = (int)H;
+  launch_gemm_mx_wgrad(b, MxOperands{m.a.s, m.b.s, (int)I, nullptr, nullptr}, EPI_F32, s);
+}
+
+void gemm_wgrad_gate_up_mx(const uint16_t *X, const uint16_t *dh, const int32_t *offsets,
+                           const int32_t *order, int G, long H, long I, float *dWg, float *dWu,
+                           const MxWgrad &m, hipStream_t s) {
+  launch_quant_cols_mx(X, 0, (int)H, offsets, m.poff, G, m.Rp, m.a.q, m.a.s, s);
+  launch_quant_cols_mx(dh, 0, (int)(2 * I), offsets, m.poff, G, m.Rp, m.b.q, m.b.s, s);
+  GemmArgs e{};
+  e.A = (const uint16_t *)m.a.q; e.lda = m.Rp;
+  e.B = (const uint16_t *)m.b.q; e.ldb = m.Rp;
+  e.C = dWg; e.C2 = dWu; e.ldc = I; e.sC = H * I;
+  e.offsets = m.poff; e.order = order;
+  e.G = G; e.M = (int)H; e.N = (int)(2 * I);
+  launch_gemm_mx_wgrad(e, MxOperands{m.a.s, m.b.s, (int)H, nullptr, nullptr}, EPI_WGRAD_GU, s);
+}
+
+// Either weight-gradient form (mxw == nullptr: bf16).
+void wgrad_down_any(const uint16_t *act, const uint16_t *dY, const int32_t *offsets,
+                    const int32_t *order, int G, long H, long I, float *dWd, const MxWgrad *mxw,
+                    hipStream_t s) {
+  if (mxw) gemm_wgrad_down_mx(act, dY, offsets, order, G, H, I, dWd, *mxw, s);
+  else gemm_wgrad_down(act, dY, offsets, order, G, H, I, dWd, s);
+}
+
+void wgrad_gate_up_any(const uint16_t *X, const uint16_t *dh, const int32_t *offsets,
+                       const int32_t *order, int G, long H, long I, float *dWg, float *dWu,
+                       const MxWgrad *mxw, hipStream_t s) {
+  if (mxw) gemm_wgrad_gate_up_mx(X, dh, offsets, order, G, H, I, dWg, dWu, *mxw, s);
+  else gemm_wgrad_gate_up(X, dh, offsets, order, G, H, I, dWg, dWu, s);
+}
+
 // The whole expert-FFN backward over row-ragged groups, given dY (rows'
 // output gradient, bf16, [rows][H]).
 void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
                   const int32_t *tiles, const int32_t *order, int G, long max_rows, long H,
                   long I, const WSet &W, bool mx, MxT dyq, MxT dhq, const uint16_t *gu_saved,
                   const uint16_t *act, uint16_t *dh, uint16_t *dX, float *dWg, float *dWu,
-                  float *dWd, hipStream_t s, const Stages *st = nullptr, int mark = 0) {
+                  float *dWd, hipStream_t s, const Stages *st = nullptr, int mark = 0,
+                  const MxWgrad *mxw = nullptr) {
   if (mx) launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
   gemm_dgrad_down(dY, dyq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, gu_saved, dh, s);
   if (st) st->mark(mark);
-  gemm_wgrad_down(act, dY, offsets, order, G, H, I, dWd, s);
+  wgrad_down_any(act, dY, offsets, order, G, H, I, dWd, mxw, s);
   if (st) st->mark(mark + 1);
   if (mx) launch_quant_rows_mx(dh, (int)max_rows, (int)(2 * I), dhq.q, dhq.s, s);
   gemm_dgrad_gate_up(dh, dhq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, dX, s);
   if (st) st->mark(mark + 2);
-  gemm_wgrad_gate_up(X, dh, offsets, order, G, H, I, dWg, dWu, s);
+  wgrad_gate_up_any(X, dh, offsets, order, G, H, I, dWg, dWu, mxw, s);
   if (st) st->mark(mark + 3);
 }
 
@@ -739,9 +807,12 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
     hipStream_t q = r->gemm[0];
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, q);
     float *dWsg = dws, *dWsu = dws + d.H * d.Is, *dWsd = dws + 2 * d.H * d.Is;
+    const MxWgrad mxs{w.poff_s, w.Rp_s, w.wq_as, w.wq_bs};
+    const bool mxw_s = d.mx && sc->mx_wgrad;
+    if (mxw_s) launch_pad_offsets(w.dense_offsets, 1, w.poff_s, q);
     ffn_backward(d.mx ? sv.xhat_s : x, dout, w.dense_offsets, w.dense_tiles, w.dense_order, 1,
                  d.T, d.H, d.Is, p.s, d.mx, w.doutq, w.dhq_s, sv.gu_s, sv.act_s, w.dh_s, w.dxs,
-                 dWsg, dWsu, dWsd, q);
+                 dWsg, dWsu, dWsd, q, nullptr, 0, mxw_s ? &mxs : nullptr);
   }
   auto rows_of = [&](int m) { return (int)std::min(MB, d.R - (long)m * MB); };
   auto RC = [&](int m) {
@@ -780,9 +851,12 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   // RC(0) is (in order on comm), every dh once the walk's last dgrad-down is
   hipStream_t q = r->gemm[1];
   if (!c.wait(q, evRC + 0)) return MOE_ERR_HIP;
-  gemm_wgrad_down(sv.act, w.dy, sv.offsets, sv.order, E, d.H, d.I, dw_down, q);
+  const MxWgrad mxw{w.poff, w.Rp, w.wq_a, w.wq_b};
+  const MxWgrad *pm = (d.mx && sc->mx_wgrad) ? &mxw : nullptr;
+  if (pm) launch_pad_offsets(sv.offsets, E, w.poff, q);
+  wgrad_down_any(sv.act, w.dy, sv.offsets, sv.order, E, d.H, d.I, dw_down, pm, q);
   if (!c.wait(q, evDD)) return MOE_ERR_HIP;
-  gemm_wgrad_gate_up(sv.x_perm, w.dh, sv.offsets, sv.order, E, d.H, d.I, dw_gate, dw_up, q);
+  wgrad_gate_up_any(sv.x_perm, w.dh, sv.offsets, sv.order, E, d.H, d.I, dw_gate, dw_up, pm, q);
   if (!c.join(evX + 1)) return MOE_ERR_HIP;
   return hip_status();
 }
@@ -1088,15 +1162,20 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
                          s);
   st.mark(1);
   // Expert FFN backward
+  const bool mxw_on = d.mx && sched && sched->mx_wgrad;
+  const MxWgrad mxw{w.poff, w.Rp, w.wq_a, w.wq_b};
+  if (mxw_on) launch_pad_offsets(sv.offsets, E, w.poff, s);
   ffn_backward(sv.x_perm, w.dy, sv.offsets, sv.tile_start, sv.order, E, d.R, d.H, d.I, p.r,
                d.mx, w.dyq, w.dhq, sv.gu, sv.act, w.dh, w.dX, dw_gate, dw_up, dw_down, s, &st,
-               2);
+               2, mxw_on ? &mxw : nullptr);
   if (d.shared) {
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
     float *dWsg = dws, *dWsu = dws + d.H * d.Is, *dWsd = dws + 2 * d.H * d.Is;
+    const MxWgrad mxs{w.poff_s, w.Rp_s, w.wq_as, w.wq_bs};
+    if (mxw_on) launch_pad_offsets(w.dense_offsets, 1, w.poff_s, s);
     ffn_backward(d.mx ? sv.xhat_s : x, dout, w.dense_offsets, w.dense_tiles, w.dense_order, 1,
                  d.T, d.H, d.Is, p.s, d.mx, w.doutq, w.dhq_s, sv.gu_s, sv.act_s, w.dh_s, w.dxs,
-                 dWsg, dWsu, dWsd, s);
+                 dWsg, dWsu, dWsd, s, nullptr, 0, mxw_on ? &mxs : nullptr);
   }
   st.mark(6);
   // Router backward and reverse-dispatch
@@ -1162,6 +1241,21 @@ int moe_decode_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_
   }
   launch_combine(w.dX, wts, w.dec_inv, d.shared ? w.dxs : nullptr, out, T, k, H, s);
   return hip_status();
+}
+
+int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view) {
+  if (!view) return MOE_ERR_INVALID_ARG;
+  *view = moe_work_view{};
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  Work w;
+  carve_work(d, ws, &w);
+  view->dy = w.dy;
+  view->dh = w.dh;
+  view->dx_rows = w.dX;
+  return MOE_OK;
 }
 
 int moe_read_status(const void *ws, int32_t *status_host, void *stream) {

@@ -40,4 +40,117 @@ void launch_gemm_rows_mx(const GemmArgs &p0, const MxOperands &mx, int epi, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// MX weight gradients.  The weight-gradient GEMMs contract over each
+// expert's routed rows, so their MX operands are quantised down the rows:
+// E8M0 blocks of 32 consecutive rows of one column, starting at the expert's
+// first row, the last block zero-padded.  Both operands are stored
+// transposed, [C][Rp] codes (row c = column c of the source, contraction
+// contiguous) with K-blocked scales [Rp/128][C][4], and each expert's row
+// segment is padded to a multiple of 128 (one GEMM stage), so that expert e
+// owns contraction range [poff[e], poff[e+1]) and the MX row tile runs on
+// it unchanged.
+
+// poff[e] = sum over e' < e of the expert row counts rounded up to 128
+// (one workgroup of 1024 threads, E <= 1024).
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t *__restrict__ offsets,
+                                                           int E, int32_t *__restrict__ poff) {
+  __shared__ int32_t sc[1024];
+  const int e = threadIdx.x;
+  const int n = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int v = (n + MXK - 1) / MXK * MXK;
+  sc[e] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+    const int add = e >= o ? sc[e - o] : 0;
+    __syncthreads();
+    v += add;
+    sc[e] = v;
+    __syncthreads();
+  }
+  if (e < E) poff[e + 1] = v;
+  if (e == 0) poff[0] = 0;
+}
+
+// Thread = (column c, 32-row block b of the padded row space): reads the
+// block's rows of column c (zeros past the expert's rows), converts them as
+// one MX block, writes 32 codes to q[c][32b ..] and the scale byte.
+__global__ __launch_bounds__(128) void quant_cols_mx_kernel(
+    const uint16_t *__restrict__ src, int C, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ poff, int E, long Rp, uint8_t *__restrict__ q,
+    uint8_t *__restrict__ sc) {
+  const int c = blockIdx.x * 128 + threadIdx.x;
+  const int b = blockIdx.y, kp = b * 32;
+  if (c >= C || kp >= poff[E]) return;
+  int lo = 0, hi = E;  // poff[lo] <= kp < poff[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (poff[mid] <= kp) lo = mid; else hi = mid;
+  }
+  const int r0 = offsets[lo] + (kp - poff[lo]), rend = offsets[lo + 1];
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; i++)
+    v[i] = r0 + i < rend ? bf16_to_f32(src[(size_t)(r0 + i) * C + c]) : 0.0f;
+  uint32_t w[8];
+  const uint32_t s = mx_block32(v, w, nullptr);
+  uint4 *dst = (uint4 *)(q + (size_t)c * Rp + kp);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  sc[((size_t)(b >> 2) * C + c) * 4 + (b & 3)] = (uint8_t)s;
+}
+
+// One 256 x 256 tile of expert order[gi]'s weight gradient C_e[M][N] =
+// A_e^T B_e over its padded contraction range.
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_mx_wgrad_kernel(GemmArgs p, MxOperands mx) {
+  __shared__ __attribute__((aligned(1024))) uint8_t L0[2 * BM * MXK];
+  __shared__ __attribute__((aligned(1024))) uint8_t L1[2 * BM * MXK];
+  const int per = p.n_tiles_m * p.n_tiles_n;
+  const int gi = blockIdx.x / per;
+  const int rem = blockIdx.x - gi * per;
+  const int g = p.order ? p.order[gi] : gi;
+  const int mt = rem / p.n_tiles_n, nt = rem - mt * p.n_tiles_n;
+  const int kp = p.offsets[g], Kp = p.offsets[g + 1] - kp;
+  GemmArgs q = p;
+  q.A = (const uint16_t *)((const uint8_t *)p.A + kp);
+  q.B = (const uint16_t *)((const uint8_t *)p.B + kp);
+  q.K = Kp;
+  q.G = 1;
+  q.sB = 0;
+  q.C = (float *)p.C + (size_t)g * p.sC;
+  q.C2 = p.C2 ? (void *)((float *)p.C2 + (size_t)g * p.sC) : nullptr;
+  MxOperands m = mx;
+  m.a_scale = mx.a_scale + (size_t)(kp / MXK) * p.M * 4;
+  m.b_scale = mx.b_scale + (size_t)(kp / MXK) * p.N * 4;
+  m.a_rows = p.M;
+  mx_tile<EPI>(q, m, 0, mt * BM, nt * BN, 0, p.M, L0, L1);
+}
+
+void launch_pad_offsets(const int32_t *offsets, int E, int32_t *poff, hipStream_t s) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, poff);
+}
+
+void launch_quant_cols_mx(const uint16_t *src, int R, int C, const int32_t *offsets,
+                          const int32_t *poff, int E, long Rp, uint8_t *q, uint8_t *sc,
+                          hipStream_t s) {
+  (void)R;
+  if (C <= 0 || Rp <= 0) return;
+  hipLaunchKernelGGL(quant_cols_mx_kernel, dim3((C + 127) / 128, (unsigned)(Rp / 32)), dim3(128),
+                     0, s, src, C, offsets, poff, E, Rp, q, sc);
+}
+
+void launch_gemm_mx_wgrad(const GemmArgs &p0, const MxOperands &mx, int epi, hipStream_t s) {
+  GemmArgs p = p0;
+  p.n_tiles_m = (p.M + BM - 1) / BM;
+  p.n_tiles_n = (p.N + BN - 1) / BN;
+  const long grid = (long)p.G * p.n_tiles_m * p.n_tiles_n;
+  if (grid <= 0) return;
+  const dim3 gr((unsigned)grid), b(NT);
+  if (epi == EPI_F32)
+    hipLaunchKernelGGL(gemm_mx_wgrad_kernel<EPI_F32>, gr, b, 0, s, p, mx);
+  else
+    hipLaunchKernelGGL(gemm_mx_wgrad_kernel<EPI_WGRAD_GU>, gr, b, 0, s, p, mx);
+}
+
 }  // namespace moe

@@ -144,6 +144,21 @@ struct MxOperands {
 void launch_gemm_rows_mx(const GemmArgs &p, const MxOperands &mx, int epi, int max_rows,
                          hipStream_t s);
 
+// MX weight gradients (gemm_mx.hip).  poff[e] = prefix of the expert row
+// counts rounded up to 128 (launch_pad_offsets); launch_quant_cols_mx
+// quantises src [R][C] bf16 down its rows in 32-row blocks per expert
+// segment into transposed codes q [C][Rp] with K-blocked scales
+// [Rp/128][C][4] (Rp: the row stride, a multiple of 128 >= poff[E]);
+// launch_gemm_mx_wgrad: C_g[M][N] = A_g^T B_g with A = transposed codes
+// [M][Rp], B = [N][Rp] (p.lda = p.ldb = Rp), group g's contraction range
+// [poff[g], poff[g+1]) (p.offsets = poff), p.order, fp32 epilogue (EPI_F32
+// or EPI_WGRAD_GU), mx.a_scale / mx.b_scale the two scale planes.
+void launch_pad_offsets(const int32_t *offsets, int E, int32_t *poff, hipStream_t s);
+void launch_quant_cols_mx(const uint16_t *src, int R, int C, const int32_t *offsets,
+                          const int32_t *poff, int E, long Rp, uint8_t *q, uint8_t *sc,
+                          hipStream_t s);
+void launch_gemm_mx_wgrad(const GemmArgs &p, const MxOperands &mx, int epi, hipStream_t s);
+
 // Weight-gradient grouped GEMM: for group g, C_g[M][N] = sum over rows
 // [offsets[g], offsets[g+1]) of A[row][M]^T B[row][N] (both row-major with the
 // summed rows outermost).

@@ -331,6 +331,9 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
       tile_epi_swiglu<true>(p, &mx, acc, L0, L1, t);
     else
       tile_epi_swiglu<false>(p, nullptr, acc, L0, L1, t);
+  } else if constexpr (EPI == EPI_F32 || EPI == EPI_WGRAD_GU) {
+    // weight gradients (fp32, p.C / p.C2 already at the group's matrix)
+    epilogue<true, EPI>(p, acc, 0, m0, n0, 0, Mg, wm0, wn0, lane);
   } else {
     tile_epi_swiglu_bwd(p, acc, L0, L1, t);
   }

@@ -85,5 +85,18 @@ class MoeLayer:
         nbytes = n * torch.empty((), dtype=dtype).element_size()
         return self.saved[off:off + nbytes].view(dtype).view(*shape)
 
+    def work_tensor(self, name: str, dtype, shape) -> torch.Tensor:
+        """A view of a backward intermediate left in the workspace (dy, dh,
+        dx_rows), valid until the next call that uses this layer's workspace."""
+        ptr = _lib.moe_workspace_pointers(self.shape, self.ws)[name]
+        if not ptr:
+            raise KeyError(name)
+        off = ptr - self.ws.data_ptr()
+        n = 1
+        for d in shape:
+            n *= d
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype).view(*shape)
+
     def status(self) -> int:
         return _lib.moe_read_status(self.ws)
