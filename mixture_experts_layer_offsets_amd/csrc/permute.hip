@@ -212,21 +212,25 @@ void launch_quant_rows_mx_range(const uint16_t *src, int row0, int rows, int row
 // Combine + final weighted fusion: out[t] = sum_j w[t,j] y[inv[t*k+j]] (+ ys[t]),
 // fp32 fused multiply-adds in ascending j.  Grid (chunk groups, T).
 
+template <int KMAX>
 __global__ __launch_bounds__(128) void combine_kernel(const uint16_t *__restrict__ y,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv,
                                                       const uint16_t *__restrict__ ys,
                                                       uint16_t *__restrict__ out, int k, int HC) {
   const int c = blockIdx.x * 128 + threadIdx.x;
-  if (c < HC) combine8(y, w, inv, ys, out, blockIdx.y, c, k, HC);
+  if (c < HC) combine8<KMAX>(y, w, inv, ys, out, blockIdx.y, c, k, HC);
 }
 
 void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,
                     uint16_t *out, int T, int k, int H, hipStream_t s) {
   const int HC = H / 8;
   if (T <= 0) return;
-  hipLaunchKernelGGL(combine_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
-                     y, w, inv, ys, out, k, HC);
+  const dim3 g((HC + 127) / 128, T), b(128);
+  if (k <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, g, b, 0, s, y, w, inv, ys, out, k, HC);
+  else
+    hipLaunchKernelGGL(combine_kernel<kCombineMaxK>, g, b, 0, s, y, w, inv, ys, out, k, HC);
 }
 
 // ---------------------------------------------------------------------------
@@ -237,19 +241,21 @@ void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const
 
 constexpr int kMaxTopK = 16;
 
+// KMAX bounds k (see combine8): 8 for k <= 8, else kMaxTopK.
+template <int KMAX>
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const uint4 *__restrict__ dout, const uint4 *__restrict__ y, const float *__restrict__ w,
     const int32_t *__restrict__ inv, uint4 *__restrict__ dy, float *__restrict__ dw,
     float *__restrict__ dsel, int k, int HC) {
-  __shared__ float red[kMaxTopK][4];
+  __shared__ float red[KMAX][4];
   const int t = blockIdx.x, tid = threadIdx.x;
-  float part[kMaxTopK];
+  float part[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) part[j] = 0.0f;
-  int rows[kMaxTopK];
-  float wt[kMaxTopK];
+  for (int j = 0; j < KMAX; j++) part[j] = 0.0f;
+  int rows[KMAX];
+  float wt[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) {  // slots past k repeat the last one, unused
+  for (int j = 0; j < KMAX; j++) {  // slots past k repeat the last one, unused
     rows[j] = inv[t * k + min(j, k - 1)];
     wt[j] = w[t * k + min(j, k - 1)];
   }
@@ -260,9 +266,9 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bool has1 = c0 + 256 < HC;
     const uint4 d0 = dout[(size_t)t * HC + c0];
     const uint4 d1 = has1 ? dout[(size_t)t * HC + c0 + 256] : make_uint4(0, 0, 0, 0);
-    uint4 yv[kMaxTopK][2];
+    uint4 yv[KMAX][2];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; j++) {
+    for (int j = 0; j < KMAX; j++) {
       if (j < k) {
         yv[j][0] = y[(size_t)rows[j] * HC + c0];
         if (has1) yv[j][1] = y[(size_t)rows[j] * HC + c0 + 256];
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
       float d[8];
       unpack8(u ? d1 : d0, d);
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; j++) {
+      for (int j = 0; j < KMAX; j++) {
         if (j < k) {
           float v[8], o[8];
           unpack8(yv[j][u], v);
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
     }
   }
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) {
+  for (int j = 0; j < KMAX; j++) {
     if (j < k) {
       const float s = wave_sum(part[j]);
       if ((tid & 63) == 0) red[j][tid >> 6] = s;
@@ -314,8 +320,13 @@ void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float
                             const int32_t *inv, uint16_t *dy, float *dw, float *dsel, int T,
                             int k, int H, hipStream_t s) {
   if (T <= 0) return;
-  hipLaunchKernelGGL(reverse_combine_kernel, dim3(T), dim3(256), 0, s, (const uint4 *)dout,
-                     (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k, H / 8);
+  if (k <= 8)
+    hipLaunchKernelGGL(reverse_combine_kernel<8>, dim3(T), dim3(256), 0, s, (const uint4 *)dout,
+                       (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k, H / 8);
+  else
+    hipLaunchKernelGGL(reverse_combine_kernel<kMaxTopK>, dim3(T), dim3(256), 0, s,
+                       (const uint4 *)dout, (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k,
+                       H / 8);
 }
 
 // ---------------------------------------------------------------------------

@@ -11,29 +11,33 @@ constexpr int kCombineMaxK = 16;  // top-k bound of the library
 // out[t] = sum_j w[t,j] y[inv[t*k+j]] (+ ys[t]), fp32 fused multiply-adds in
 // ascending j, rounded to bf16 once.  All k rows' chunks are loaded before
 // the first multiply-add, so one memory round trip covers the token.
+// KMAX bounds k (8 or kCombineMaxK): the per-slot arrays take KMAX registers
+// each, so the k <= 8 instantiation runs with far fewer registers (more
+// waves in flight); the arithmetic is the same for every KMAX >= k.
+template <int KMAX = kCombineMaxK>
 __device__ __forceinline__ void combine8(const uint16_t *y, const float *w, const int32_t *inv,
                                          const uint16_t *ys, uint16_t *out, int t, int c, int k,
                                          int HC) {
   // row indices and weights first, unconditionally (slots past k repeat the
   // last one), so their loads issue together rather than one per row load
-  int row[kCombineMaxK];
-  float wt[kCombineMaxK];
+  int row[KMAX];
+  float wt[KMAX];
 #pragma unroll
-  for (int j = 0; j < kCombineMaxK; j++) {
+  for (int j = 0; j < KMAX; j++) {
     row[j] = inv[t * k + min(j, k - 1)];
     wt[j] = w[t * k + min(j, k - 1)];
   }
   // (needed here: keeps the compiler from sinking each index load next to
   // its row load)
 #pragma unroll
-  for (int j = 0; j < kCombineMaxK; j++) asm volatile("" ::"v"(row[j]));
-  uint4 rv[kCombineMaxK];
+  for (int j = 0; j < KMAX; j++) asm volatile("" ::"v"(row[j]));
+  uint4 rv[KMAX];
 #pragma unroll
-  for (int j = 0; j < kCombineMaxK; j++)
+  for (int j = 0; j < KMAX; j++)
     if (j < k) rv[j] = ((const uint4 *)y)[(size_t)row[j] * HC + c];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int j = 0; j < kCombineMaxK; j++) {
+  for (int j = 0; j < KMAX; j++) {
     if (j < k) {
       const float wj = wt[j];
       float v[8];
