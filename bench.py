@@ -116,6 +116,10 @@ def _algorithmic(w):
         # dOut read once, Y read for dw, dY written, + weights/indices/dw
         "reverse_combine": T * H * 2 + 2 * R * H * 2 + R * 12,
     }
+    if w.routing == "supplied":
+        # without a router this stage is reverse-dispatch alone: the rows'
+        # gradients read once, token rows written once, + indices
+        b["router_bwd+reverse_dispatch"] = R * H * 2 + T * H * 2 + R * 4
     return f, b
 
 

@@ -333,6 +333,10 @@ void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float
 // Reverse-dispatch: dx[t] = sum_j dX[inv[t*k+j]] + sum_j dsel[t,j] Wr^T[idx[t,j]]
 // (+ dxs[t]), fp32 in ascending j, stored as bf16.
 
+// KMAX bounds k (see combine8); ROUTER / SHARED: whether the router term and
+// the shared expert's rows exist (the kernel without them carries neither
+// branch nor their registers).
+template <int KMAX, bool ROUTER, bool SHARED>
 __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
     const uint4 *__restrict__ dX, const int32_t *__restrict__ inv, const int32_t *__restrict__ idx,
     const float *__restrict__ dsel, const uint4 *__restrict__ wrT, const uint4 *__restrict__ dxs,
@@ -342,18 +346,18 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
   if (c >= HC) return;
   // all k row indices, then all k rows' chunks, in flight before the first
   // add (index slots past k repeat the last one)
-  int row[kMaxTopK];
+  int row[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) row[j] = inv[t * k + min(j, k - 1)];
+  for (int j = 0; j < KMAX; j++) row[j] = inv[t * k + min(j, k - 1)];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) asm volatile("" ::"v"(row[j]));  // materialise here
-  uint4 rv[kMaxTopK];
+  for (int j = 0; j < KMAX; j++) asm volatile("" ::"v"(row[j]));  // materialise here
+  uint4 rv[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++)
+  for (int j = 0; j < KMAX; j++)
     if (j < k) rv[j] = dX[(size_t)row[j] * HC + c];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; j++) {
+  for (int j = 0; j < KMAX; j++) {
     if (j < k) {
       float v[8];
       unpack8(rv[j], v);
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
       for (int q = 0; q < 8; q++) acc[q] += v[q];
     }
   }
-  if (wrT) {
+  if constexpr (ROUTER) {
     for (int j = 0; j < k; j++) {
       const float sj = dsel[t * k + j];
       float v[8];
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
       for (int q = 0; q < 8; q++) acc[q] = fmaf(sj, v[q], acc[q]);
     }
   }
-  if (dxs) {
+  if constexpr (SHARED) {
     float v[8];
     unpack8(dxs[(size_t)t * HC + c], v);
 #pragma unroll
@@ -379,14 +383,39 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
   dx[(size_t)t * HC + c] = pack8(acc);
 }
 
+template <int KMAX>
+static void launch_rd(const dim3 &g, const uint16_t *dX, const int32_t *inv, const int32_t *idx,
+                      const float *dsel, const uint16_t *wrT, const uint16_t *dxs, uint16_t *dx,
+                      int k, int HC, hipStream_t s) {
+  const dim3 b(128);
+  auto *X = (const uint4 *)dX;
+  auto *W = (const uint4 *)wrT;
+  auto *S = (const uint4 *)dxs;
+  auto *D = (uint4 *)dx;
+  if (wrT && dxs)
+    hipLaunchKernelGGL((reverse_dispatch_kernel<KMAX, true, true>), g, b, 0, s, X, inv, idx, dsel,
+                       W, S, D, k, HC);
+  else if (wrT)
+    hipLaunchKernelGGL((reverse_dispatch_kernel<KMAX, true, false>), g, b, 0, s, X, inv, idx,
+                       dsel, W, S, D, k, HC);
+  else if (dxs)
+    hipLaunchKernelGGL((reverse_dispatch_kernel<KMAX, false, true>), g, b, 0, s, X, inv, idx,
+                       dsel, W, S, D, k, HC);
+  else
+    hipLaunchKernelGGL((reverse_dispatch_kernel<KMAX, false, false>), g, b, 0, s, X, inv, idx,
+                       dsel, W, S, D, k, HC);
+}
+
 void launch_reverse_dispatch(const uint16_t *dX, const int32_t *inv, const int32_t *idx,
                              const float *dsel, const uint16_t *wrT, const uint16_t *dxs,
                              uint16_t *dx, int T, int k, int H, hipStream_t s) {
   const int HC = H / 8;
   if (T <= 0) return;
-  hipLaunchKernelGGL(reverse_dispatch_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
-                     (const uint4 *)dX, inv, idx, dsel, (const uint4 *)wrT, (const uint4 *)dxs,
-                     (uint4 *)dx, k, HC);
+  const dim3 g((HC + 127) / 128, T);
+  if (k <= 8)
+    launch_rd<8>(g, dX, inv, idx, dsel, wrT, dxs, dx, k, HC, s);
+  else
+    launch_rd<kMaxTopK>(g, dX, inv, idx, dsel, wrT, dxs, dx, k, HC, s);
 }
 
 // ---------------------------------------------------------------------------
