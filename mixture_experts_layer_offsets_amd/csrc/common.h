@@ -46,6 +46,14 @@ __device__ __forceinline__ uint4 pack8(const float *f) {
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// A 16-byte load of data read exactly once (non-temporal: it does not
+// displace cache lines that will be read again).
+__device__ __forceinline__ uint4 ld_once(const uint4 *p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Wave-wide sum (fixed butterfly order -> deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

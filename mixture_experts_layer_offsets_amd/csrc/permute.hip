@@ -110,7 +110,9 @@ void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uin
 // token once instead of k times.  Grid (H/8 chunks over 128 threads, T).
 
 // Only rows in [r0, r1) are written (one minibatch of sorted rows; the whole
-// set is [0, T*k)).
+// set is [0, T*k)).  KMAX bounds k (8 or kMaxTopKPush): no index loads past
+// the bound.
+template <int KMAX>
 __global__ __launch_bounds__(128) void dispatch_push_bf16_kernel(const uint4 *__restrict__ x,
                                                                  const int32_t *__restrict__ inv,
                                                                  uint4 *__restrict__ xp, int k,
@@ -118,17 +120,17 @@ __global__ __launch_bounds__(128) void dispatch_push_bf16_kernel(const uint4 *__
   const int t = blockIdx.y;
   const int c = blockIdx.x * 128 + threadIdx.x;
   if (c >= HC) return;
-  int row[kMaxTopKPush];
+  int row[KMAX];
   bool any = false;
 #pragma unroll
-  for (int j = 0; j < kMaxTopKPush; j++) {
+  for (int j = 0; j < KMAX; j++) {
     row[j] = inv[t * k + min(j, k - 1)];
     any |= j < k && row[j] >= r0 && row[j] < r1;
   }
   if (!any) return;
-  const uint4 v = x[(size_t)t * HC + c];
+  const uint4 v = ld_once(x + (size_t)t * HC + c);
 #pragma unroll
-  for (int j = 0; j < kMaxTopKPush; j++)
+  for (int j = 0; j < KMAX; j++)
     if (j < k && row[j] >= r0 && row[j] < r1) xp[(size_t)row[j] * HC + c] = v;
 }
 
@@ -136,8 +138,13 @@ void launch_dispatch_push_bf16_range(const uint16_t *x, const int32_t *inv, uint
                                      int k, int H, int r0, int r1, hipStream_t s) {
   const int HC = H / 8;
   if (T <= 0) return;
-  hipLaunchKernelGGL(dispatch_push_bf16_kernel, dim3((HC + 127) / 128, T), dim3(128), 0, s,
-                     (const uint4 *)x, inv, (uint4 *)xp, k, HC, r0, r1);
+  const dim3 g((HC + 127) / 128, T), b(128);
+  if (k <= 8)
+    hipLaunchKernelGGL(dispatch_push_bf16_kernel<8>, g, b, 0, s, (const uint4 *)x, inv,
+                       (uint4 *)xp, k, HC, r0, r1);
+  else
+    hipLaunchKernelGGL(dispatch_push_bf16_kernel<kMaxTopKPush>, g, b, 0, s, (const uint4 *)x,
+                       inv, (uint4 *)xp, k, HC, r0, r1);
 }
 
 void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T, int k,
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
   }
   if (!any) return;
   float v[8];
-  unpack8(x[(size_t)t * HC + c], v);
+  unpack8(ld_once(x + (size_t)t * HC + c), v);
   uint2 codes;
   float deq[8];
   const uint32_t sc = mx_quad8(v, &codes, deq);
@@ -264,14 +271,15 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
   // ascending column order.
   for (int c0 = tid; c0 < HC; c0 += 512) {
     const bool has1 = c0 + 256 < HC;
-    const uint4 d0 = dout[(size_t)t * HC + c0];
-    const uint4 d1 = has1 ? dout[(size_t)t * HC + c0 + 256] : make_uint4(0, 0, 0, 0);
+    // dout and the k rows of y are each read once
+    const uint4 d0 = ld_once(dout + (size_t)t * HC + c0);
+    const uint4 d1 = has1 ? ld_once(dout + (size_t)t * HC + c0 + 256) : make_uint4(0, 0, 0, 0);
     uint4 yv[KMAX][2];
 #pragma unroll
     for (int j = 0; j < KMAX; j++) {
       if (j < k) {
-        yv[j][0] = y[(size_t)rows[j] * HC + c0];
-        if (has1) yv[j][1] = y[(size_t)rows[j] * HC + c0 + 256];
+        yv[j][0] = ld_once(y + (size_t)rows[j] * HC + c0);
+        if (has1) yv[j][1] = ld_once(y + (size_t)rows[j] * HC + c0 + 256);
       }
     }
 #pragma unroll
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
   uint4 rv[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; j++)
-    if (j < k) rv[j] = dX[(size_t)row[j] * HC + c];
+    if (j < k) rv[j] = ld_once(dX + (size_t)row[j] * HC + c);  // read once
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < KMAX; j++) {

@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256) void reverse_combine_rows_kernel(
     for (int u = 0; u < 4; u++) {
       const int c = c0 + 256 * u;
       if (c < HC) {
-        dv[u] = dout[(size_t)t * HC + c];
-        yv[u] = y[(size_t)r * HC + c];
+        dv[u] = ld_once(dout + (size_t)t * HC + c);
+        yv[u] = ld_once(y + (size_t)r * HC + c);
       }
     }
 #pragma unroll
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(128) void reverse_dispatch_list_kernel(
     uint4 rv[kMaxTopKList];
 #pragma unroll
     for (int j = 0; j < kMaxTopKList; j++)
-      if (j < k) rv[j] = dX[(size_t)row[j] * HC + c];
+      if (j < k) rv[j] = ld_once(dX + (size_t)row[j] * HC + c);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < kMaxTopKList; j++) {

@@ -34,7 +34,7 @@ __device__ __forceinline__ void combine8(const uint16_t *y, const float *w, cons
   uint4 rv[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; j++)
-    if (j < k) rv[j] = ((const uint4 *)y)[(size_t)row[j] * HC + c];
+    if (j < k) rv[j] = ld_once((const uint4 *)y + (size_t)row[j] * HC + c);  // read once
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < KMAX; j++) {
