@@ -65,7 +65,8 @@ def test_binding_argument_counts_match_header():
 def test_struct_layouts_match_header():
     text = open(HEADER).read()
     for cname, pyt in (("moe_shape", _lib.MoeShape), ("moe_sched", _lib.MoeSched),
-                       ("moe_saved_view", _lib.MoeSavedView)):
+                       ("moe_saved_view", _lib.MoeSavedView),
+                       ("moe_work_view", _lib.MoeWorkView)):
         body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (cname, cname), text, re.S).group(1)
         body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
         fields = re.findall(r"(\w+)\s*;", body)
@@ -153,3 +154,66 @@ def test_megakernel_request_is_refused(lib):
     fake = 1 << 40
     assert lib.moe_layer_fwd(s, ctypes.byref(sched), fake, None, None, fake, fake, fake, fake,
                              fake, fake, 1 << 40, None) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_schedule_validation(lib):
+    """An unknown schedule and a negative CU count for the pipelined schedule
+    are rejected before any device work (forward and backward)."""
+    s = ctypes.byref(m.Shape(64, 128, 8, 2, 64).c())
+    fake = 1 << 40
+    for mode, cus in ((7, 0), (-1, 0), (m.MOE_SCHED_PIPELINED, -4)):
+        sched = m.MoeSched()
+        sched.schedule = mode
+        sched.comm_cus = cus
+        assert lib.moe_layer_fwd(s, ctypes.byref(sched), fake, None, None, fake, fake, fake, fake,
+                                 fake, fake, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+        assert lib.moe_layer_bwd(s, ctypes.byref(sched), fake, fake, None, fake, fake, fake, None,
+                                 fake, fake, fake, None, None, fake, 1 << 40,
+                                 None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_decode_argument_validation(lib):
+    """moe_decode_fwd: MXFP8 shapes are refused; routing must be either the
+    router or supplied indices and weights; k > E needs supplied routing."""
+    fake = 1 << 40
+    mx = ctypes.byref(m.Shape(4, 256, 8, 2, 128, 0, m.MOE_MXFP8).c())
+    assert lib.moe_decode_fwd(mx, fake, None, None, fake, fake, fake, fake, fake, 1 << 40,
+                              None) == _lib.MOE_ERR_UNSUPPORTED
+    s = ctypes.byref(m.Shape(4, 256, 8, 2, 128).c())
+    # both a router and supplied routing
+    assert lib.moe_decode_fwd(s, fake, fake, None, fake, fake, fake, fake, fake, 1 << 40,
+                              None) == _lib.MOE_ERR_INVALID_ARG
+    # neither
+    assert lib.moe_decode_fwd(s, fake, None, None, None, None, fake, fake, fake, 1 << 40,
+                              None) == _lib.MOE_ERR_INVALID_ARG
+    # indices without weights
+    assert lib.moe_decode_fwd(s, fake, None, None, fake, None, fake, fake, fake, 1 << 40,
+                              None) == _lib.MOE_ERR_INVALID_ARG
+    # router with k > E
+    big_k = ctypes.byref(m.Shape(4, 256, 8, 9, 128).c())
+    assert lib.moe_decode_fwd(big_k, fake, fake, None, None, None, fake, fake, fake, 1 << 40,
+                              None) == _lib.MOE_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.moe_decode_fwd(s, fake, None, None, fake, fake, fake, fake, fake, 16,
+                              None) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_workspace_pointers(lib):
+    """The backward's row intermediates lie inside the workspace, disjoint,
+    at the sizes the header states."""
+    shape = m.Shape(100, 256, 6, 4, 128)
+    base = 1 << 40
+    nbytes = _lib.moe_workspace_bytes(shape)
+    view = _lib.MoeWorkView()
+    assert lib.moe_workspace_pointers(ctypes.byref(shape.c()), base,
+                                      ctypes.byref(view)) == _lib.MOE_OK
+    R, H, I = 100 * 4, 256, 128
+    spans = sorted([(view.dy, R * H * 2), (view.dh, R * 2 * I * 2), (view.dx_rows, R * H * 2)])
+    for (p, n), (q, _) in zip(spans, spans[1:]):
+        assert p + n <= q
+    for p, n in spans:
+        assert base <= p and p + n <= base + nbytes
+    bad = m.Shape(0, 256, 6, 4, 128)
+    assert lib.moe_workspace_pointers(ctypes.byref(bad.c()), base,
+                                      ctypes.byref(view)) == _lib.MOE_ERR_INVALID_ARG
+    assert view.dy is None and view.dh is None
