@@ -64,6 +64,9 @@ def _args():
                     help="schedule whose throughput is `value` (both are timed and reported)")
     ap.add_argument("--minibatch-rows", type=int, default=0,
                     help="pipelined schedule: routed rows per minibatch (0 = library default)")
+    ap.add_argument("--ring-slots", type=int, default=0,
+                    help="pipelined schedule: minibatches dispatched ahead of the gate/up GEMM "
+                         "(0 = library default)")
     ap.add_argument("--comm-cus", type=int, default=0,
                     help="pipelined schedule: CUs of the communication stream (0 = share all)")
     ap.add_argument("--sweep-minibatch", default="",
@@ -242,6 +245,7 @@ def main():
         s.schedule = m.MOE_SCHED_PIPELINED
         s.minibatch_rows = a.minibatch_rows
         s.comm_cus = a.comm_cus
+        s.ring_slots = a.ring_slots
         return s
 
     def timed_loop(sf=None, sb=None):
@@ -279,6 +283,7 @@ def main():
             q.schedule = m.MOE_SCHED_PIPELINED
             q.minibatch_rows = a.minibatch_rows
             q.comm_cus = a.comm_cus
+            q.ring_slots = a.ring_slots
         psched.append(((pf, af), (pb, ab)))
     torch.cuda.synchronize()
     for (pf, _), (pb, _) in psched:
