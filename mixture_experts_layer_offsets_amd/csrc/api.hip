@@ -716,7 +716,7 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
   // the plan (GEMM offsets, token lists) runs beside the first dispatch,
   // which needs only inv
   launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
-                   w.tlf_off, w.tlb, w.tlb_off, r->gemm[0]);
+                   w.tlf_off, nullptr, nullptr, r->gemm[0]);
   if (!c.rec(r->gemm[0], evPlan) || !c.wait(r->gemm[1], evPlan)) return MOE_ERR_HIP;
   if (d.shared) {
     hipStream_t q = r->gemm[0];
@@ -800,8 +800,8 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   // the plan (and the router's W_r^T) run on GEMM stream 0 beside the first
   // reverse-combine, which needs neither; the communication stream waits for
   // them before its first reverse-dispatch
-  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
-                   w.tlf_off, w.tlb, w.tlb_off, r->gemm[0]);
+  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, nullptr,
+                   nullptr, w.tlb, w.tlb_off, r->gemm[0]);
   if (router) launch_transpose_pack(w_router, w.wrT, 1, H, E, E, 32, 0, r->gemm[0]);
   if (d.shared) {
     hipStream_t q = r->gemm[0];

@@ -37,6 +37,8 @@ namespace moe {
 // The order of tokens inside one list is not fixed (LDS atomics place them);
 // each token's result is computed on its own, so outputs do not depend on it.
 
+// A direction needs one of the two token lists: tlf (forward) or tlb
+// (backward) may be null, and then that list is not built.
 __global__ __launch_bounds__(1024) void pipe_plan_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ inv, int T, int k, int E,
     int R, int MB, int NM, int32_t *__restrict__ moff, int32_t *__restrict__ mts,
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(1024) void pipe_plan_kernel(
     cnt_b[m] = 0;
   }
   __syncthreads();
+  const bool fwd = tlf != nullptr, bwd = tlb != nullptr;
   for (int t = tid; t < T; t += 1024) {
     int hi = 0, lo = R;
     for (int j = 0; j < k; j++) {
@@ -70,20 +73,23 @@ __global__ __launch_bounds__(1024) void pipe_plan_kernel(
       hi = max(hi, r);
       lo = min(lo, r);
     }
-    atomicAdd(&cnt_f[hi / MB], 1);
-    atomicAdd(&cnt_b[lo / MB], 1);
+    if (fwd) atomicAdd(&cnt_f[hi / MB], 1);
+    if (bwd) atomicAdd(&cnt_b[lo / MB], 1);
   }
   __syncthreads();
   if (tid == 0) {
     int sf = 0, sb = 0;
     for (int m = 0; m < NM; m++) {
-      base_f[m] = sf; tlf_off[m] = sf; sf += cnt_f[m];
-      base_b[m] = sb; tlb_off[m] = sb; sb += cnt_b[m];
+      base_f[m] = sf; sf += cnt_f[m];
+      base_b[m] = sb; sb += cnt_b[m];
     }
-    tlf_off[NM] = sf;
-    tlb_off[NM] = sb;
   }
   __syncthreads();
+  for (int m = tid; m <= NM; m += 1024) {
+    if (fwd) tlf_off[m] = m < NM ? base_f[m] : base_f[NM - 1] + cnt_f[NM - 1];
+    if (bwd) tlb_off[m] = m < NM ? base_b[m] : base_b[NM - 1] + cnt_b[NM - 1];
+  }
+  __syncthreads();  // the offsets are read from base_* before placement moves them
   for (int t = tid; t < T; t += 1024) {
     int hi = 0, lo = R;
     for (int j = 0; j < k; j++) {
@@ -91,8 +97,8 @@ __global__ __launch_bounds__(1024) void pipe_plan_kernel(
       hi = max(hi, r);
       lo = min(lo, r);
     }
-    tlf[atomicAdd(&base_f[hi / MB], 1)] = t;
-    tlb[atomicAdd(&base_b[lo / MB], 1)] = t;
+    if (fwd) tlf[atomicAdd(&base_f[hi / MB], 1)] = t;
+    if (bwd) tlb[atomicAdd(&base_b[lo / MB], 1)] = t;
   }
 }
 
