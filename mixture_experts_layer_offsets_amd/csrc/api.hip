@@ -624,21 +624,27 @@ int pipe_resources(int comm_cus, size_t n_events, PipeRes **out) {
       r.init = false;
     }
     const int cus = device_cus();
+    r.comm = r.gemm[0] = r.gemm[1] = nullptr;
+    bool ok = true;
     if (comm_cus > 0) {
       if (comm_cus >= cus) return MOE_ERR_INVALID_ARG;
-      // CU mask bits: the first comm_cus bits go to the communication stream
-      // (the driver spreads consecutive mask bits over the XCDs), the rest to
-      // the GEMM streams
+      // CU mask bits: the first comm_cus bits of the mask go to the
+      // communication stream, the rest to the GEMM streams
       std::vector<uint32_t> cm((cus + 31) / 32, 0u), gm((cus + 31) / 32, 0u);
       for (int i = 0; i < cus; i++) (i < comm_cus ? cm : gm)[i / 32] |= 1u << (i % 32);
-      if (hipExtStreamCreateWithCUMask(&r.comm, (uint32_t)cm.size(), cm.data()) != hipSuccess ||
-          hipExtStreamCreateWithCUMask(&r.gemm[0], (uint32_t)gm.size(), gm.data()) !=
-              hipSuccess ||
-          hipExtStreamCreateWithCUMask(&r.gemm[1], (uint32_t)gm.size(), gm.data()) != hipSuccess)
-        return MOE_ERR_HIP;
+      ok = hipExtStreamCreateWithCUMask(&r.comm, (uint32_t)cm.size(), cm.data()) == hipSuccess &&
+           hipExtStreamCreateWithCUMask(&r.gemm[0], (uint32_t)gm.size(), gm.data()) ==
+               hipSuccess &&
+           hipExtStreamCreateWithCUMask(&r.gemm[1], (uint32_t)gm.size(), gm.data()) == hipSuccess;
     } else {
       for (hipStream_t *q : {&r.comm, &r.gemm[0], &r.gemm[1]})
-        if (hipStreamCreateWithFlags(q, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+        ok = ok && hipStreamCreateWithFlags(q, hipStreamNonBlocking) == hipSuccess;
+    }
+    if (!ok) {  // drop whatever was created; the next call tries again
+      for (hipStream_t q : {r.comm, r.gemm[0], r.gemm[1]})
+        if (q) hipStreamDestroy(q);
+      r.comm = r.gemm[0] = r.gemm[1] = nullptr;
+      return MOE_ERR_HIP;
     }
     r.comm_cus = comm_cus;
     r.init = true;
