@@ -379,7 +379,10 @@ def main():
     traffic = _traffic(kernel, w.name)
     tokens_per_step = w.T
     res = {
-        "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X" if w.backward
+        # value is the tokens/s; the grouped-GEMM MFMA and permute HBM
+        # fractions are the roofline, mfma_frac and hbm_frac fields
+        "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM MFMA % and permute HBM %"
+                  if w.backward
                   else "MoE layer fwd tokens/s on 1 MI355X",
         "value": tokens_per_step * a.steps / elapsed,
         "unit": "tokens/s",
