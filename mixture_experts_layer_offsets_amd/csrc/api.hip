@@ -719,10 +719,10 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
   const int evD = 0, evG1 = NM, evG2 = 2 * NM, evX = 3 * NM, evPlan = 3 * NM + 4;
   const PipeCtx c{r, s};
   if (!c.fork(evX)) return MOE_ERR_HIP;
-  // the plan (GEMM offsets, token lists) runs beside the first dispatch,
-  // which needs only inv
-  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, w.tlf,
-                   w.tlf_off, nullptr, nullptr, r->gemm[0]);
+  // the minibatches' GEMM offsets run beside the first dispatch (which needs
+  // only inv); the combine's token lists follow the first dispatches on the
+  // communication stream (below)
+  launch_pipe_offsets(sv.offsets, E, R, (int)MB, NM, w.pm_off, w.pm_ts, r->gemm[0]);
   if (!c.rec(r->gemm[0], evPlan) || !c.wait(r->gemm[1], evPlan)) return MOE_ERR_HIP;
   if (d.shared) {
     hipStream_t q = r->gemm[0];
@@ -755,8 +755,6 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
     return c.rec(q, evG2 + m);
   };
   auto C = [&](int m) {
-    // down(m) follows the plan on its stream, so waiting for it covers the
-    // token lists too
     if (!c.wait(r->comm, evG2 + m) || (m > 0 && !c.wait(r->comm, evG2 + m - 1))) return false;
     launch_combine_list(sv.y, sv.w, sv.inv, d.shared ? sv.y_s : nullptr, out, w.tlf, w.tlf_off, m,
                         T, k, H, r->comm);
@@ -764,6 +762,7 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
   };
   for (int m = 0; m < std::min(S, NM); m++)
     if (!D(m)) return MOE_ERR_HIP;
+  launch_pipe_lists(sv.inv, T, k, R, (int)MB, NM, true, w.tlf, w.tlf_off, r->comm);
   for (int m = 0; m < NM; m++) {
     if (!G(m)) return MOE_ERR_HIP;
     if (m + S < NM && !D(m + S)) return MOE_ERR_HIP;
@@ -803,11 +802,12 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   const PipeCtx c{r, s};
   const bool router = w_router != nullptr;
   if (!c.fork(evX)) return MOE_ERR_HIP;
-  // the plan (and the router's W_r^T) run on GEMM stream 0 beside the first
-  // reverse-combine, which needs neither; the communication stream waits for
-  // them before its first reverse-dispatch
-  launch_pipe_plan(sv.offsets, sv.inv, T, k, E, R, (int)MB, NM, w.pm_off, w.pm_ts, nullptr,
-                   nullptr, w.tlb, w.tlb_off, r->gemm[0]);
+  // the minibatches' GEMM offsets (and the router's W_r^T) run on GEMM
+  // stream 0 beside the first reverse-combine, which needs neither; the
+  // communication stream waits for them before its first reverse-dispatch,
+  // and builds the reverse-dispatch token lists itself after the first
+  // reverse-combine (below)
+  launch_pipe_offsets(sv.offsets, E, R, (int)MB, NM, w.pm_off, w.pm_ts, r->gemm[0]);
   if (router) launch_transpose_pack(w_router, w.wrT, 1, H, E, E, 32, 0, r->gemm[0]);
   if (d.shared) {
     hipStream_t q = r->gemm[0];
@@ -839,7 +839,7 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
     return c.rec(q, evDG + m);
   };
   auto RD = [&](int m) {
-    // DG(m) follows the plan and W_r^T on GEMM stream 0
+    // DG(m) follows W_r^T on GEMM stream 0; the token lists precede RD on comm
     if (!c.wait(r->comm, evDG + m)) return false;
     launch_reverse_dispatch_list(w.dX, sv.inv, sv.idx, sv.w, dw, w.dsel,
                                  router ? w.wrT : nullptr, d.shared ? w.dxs : nullptr, dx, w.tlb,
@@ -847,6 +847,7 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
     return true;
   };
   if (!RC(NM - 1)) return MOE_ERR_HIP;
+  launch_pipe_lists(sv.inv, T, k, R, (int)MB, NM, false, w.tlb, w.tlb_off, r->comm);
   for (int m = NM - 1; m >= 0; m--) {
     if (!DG(m, r->gemm[0])) return MOE_ERR_HIP;
     if (m > 0 && !RC(m - 1)) return MOE_ERR_HIP;

@@ -66,9 +66,10 @@ void launch_interleave_copy(const uint16_t *in, uint16_t *out, int G, int rows, 
                             int out_cols, int blk_stride, int blk_off, hipStream_t s);
 
 // pipeline.hip: the minibatch schedule's plan and its per-minibatch data movement
-void launch_pipe_plan(const int32_t *offsets, const int32_t *inv, int T, int k, int E, int R,
-                      int MB, int NM, int32_t *moff, int32_t *mts, int32_t *tlf, int32_t *tlf_off,
-                      int32_t *tlb, int32_t *tlb_off, hipStream_t s);
+void launch_pipe_offsets(const int32_t *offsets, int E, int R, int MB, int NM, int32_t *moff,
+                         int32_t *mts, hipStream_t s);
+void launch_pipe_lists(const int32_t *inv, int T, int k, int R, int MB, int NM, bool last,
+                       int32_t *tl, int32_t *tl_off, hipStream_t s);
 void launch_combine_list(const uint16_t *y, const float *w, const int32_t *inv,
                          const uint16_t *ys, uint16_t *out, const int32_t *tl,
                          const int32_t *tl_off, int m, int T, int k, int H, hipStream_t s);

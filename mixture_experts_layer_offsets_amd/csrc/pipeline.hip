@@ -23,31 +23,25 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Plan (one 1024-thread workgroup):
-//   moff[m][e]  = offsets[e] clamped to minibatch m's row range (so expert e
-//                 owns rows [moff[m][e], moff[m][e+1]) of minibatch m);
-//   mts[m][e]   = prefix of the 256-row tiles of those ranges (the grouped
-//                 GEMM's tile_start for minibatch m);
-//   tlf / tlf_off: tokens grouped by the minibatch holding their LAST routed
-//                 row (the forward combines a token once that minibatch's
-//                 down projection is done);
-//   tlb / tlb_off: tokens grouped by the minibatch holding their FIRST routed
-//                 row (the reverse walk has all of a token's row gradients
-//                 once that minibatch is done).
+// Plan, in two kernels (one workgroup of 1024 threads each), so that the
+// GEMMs wait only for the first:
+//   offsets: moff[m][e] = offsets[e] clamped to minibatch m's row range (so
+//            expert e owns rows [moff[m][e], moff[m][e+1]) of minibatch m);
+//            mts[m][e] = prefix of the 256-row tiles of those ranges (the
+//            grouped GEMM's tile_start for minibatch m);
+//   lists:   tl / tl_off: tokens grouped by the minibatch holding their LAST
+//            routed row (last = 1: the forward combines a token once that
+//            minibatch's down projection is done) or their FIRST routed row
+//            (last = 0: the reverse walk has all of a token's row gradients
+//            once that minibatch is done).
 // The order of tokens inside one list is not fixed (LDS atomics place them);
 // each token's result is computed on its own, so outputs do not depend on it.
 
-// A direction needs one of the two token lists: tlf (forward) or tlb
-// (backward) may be null, and then that list is not built.
-__global__ __launch_bounds__(1024) void pipe_plan_kernel(
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ inv, int T, int k, int E,
-    int R, int MB, int NM, int32_t *__restrict__ moff, int32_t *__restrict__ mts,
-    int32_t *__restrict__ tlf, int32_t *__restrict__ tlf_off, int32_t *__restrict__ tlb,
-    int32_t *__restrict__ tlb_off) {
-  __shared__ int cnt_f[kPipeMaxMinibatches], cnt_b[kPipeMaxMinibatches];
-  __shared__ int base_f[kPipeMaxMinibatches], base_b[kPipeMaxMinibatches];
-  const int tid = threadIdx.x;
-  for (int m = tid; m < NM; m += 1024) {
+__global__ __launch_bounds__(1024) void pipe_offsets_kernel(const int32_t *__restrict__ offsets,
+                                                            int E, int R, int MB, int NM,
+                                                            int32_t *__restrict__ moff,
+                                                            int32_t *__restrict__ mts) {
+  for (int m = threadIdx.x; m < NM; m += 1024) {
     const int lo = m * MB, hi = min(R, lo + MB);
     int32_t *mo = moff + (size_t)m * (E + 1), *mt = mts + (size_t)m * (E + 1);
     int tiles = 0;
@@ -61,52 +55,49 @@ __global__ __launch_bounds__(1024) void pipe_plan_kernel(
       prev = nxt;
     }
     mt[E] = tiles;
-    cnt_f[m] = 0;
-    cnt_b[m] = 0;
-  }
-  __syncthreads();
-  const bool fwd = tlf != nullptr, bwd = tlb != nullptr;
-  for (int t = tid; t < T; t += 1024) {
-    int hi = 0, lo = R;
-    for (int j = 0; j < k; j++) {
-      const int r = inv[t * k + j];
-      hi = max(hi, r);
-      lo = min(lo, r);
-    }
-    if (fwd) atomicAdd(&cnt_f[hi / MB], 1);
-    if (bwd) atomicAdd(&cnt_b[lo / MB], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int sf = 0, sb = 0;
-    for (int m = 0; m < NM; m++) {
-      base_f[m] = sf; sf += cnt_f[m];
-      base_b[m] = sb; sb += cnt_b[m];
-    }
-  }
-  __syncthreads();
-  for (int m = tid; m <= NM; m += 1024) {
-    if (fwd) tlf_off[m] = m < NM ? base_f[m] : base_f[NM - 1] + cnt_f[NM - 1];
-    if (bwd) tlb_off[m] = m < NM ? base_b[m] : base_b[NM - 1] + cnt_b[NM - 1];
-  }
-  __syncthreads();  // the offsets are read from base_* before placement moves them
-  for (int t = tid; t < T; t += 1024) {
-    int hi = 0, lo = R;
-    for (int j = 0; j < k; j++) {
-      const int r = inv[t * k + j];
-      hi = max(hi, r);
-      lo = min(lo, r);
-    }
-    if (fwd) tlf[atomicAdd(&base_f[hi / MB], 1)] = t;
-    if (bwd) tlb[atomicAdd(&base_b[lo / MB], 1)] = t;
   }
 }
 
-void launch_pipe_plan(const int32_t *offsets, const int32_t *inv, int T, int k, int E, int R,
-                      int MB, int NM, int32_t *moff, int32_t *mts, int32_t *tlf, int32_t *tlf_off,
-                      int32_t *tlb, int32_t *tlb_off, hipStream_t s) {
-  hipLaunchKernelGGL(pipe_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, inv, T, k, E, R, MB,
-                     NM, moff, mts, tlf, tlf_off, tlb, tlb_off);
+__global__ __launch_bounds__(1024) void pipe_lists_kernel(const int32_t *__restrict__ inv, int T,
+                                                          int k, int R, int MB, int NM, int last,
+                                                          int32_t *__restrict__ tl,
+                                                          int32_t *__restrict__ tl_off) {
+  __shared__ int cnt[kPipeMaxMinibatches], base[kPipeMaxMinibatches];
+  const int tid = threadIdx.x;
+  for (int m = tid; m < NM; m += 1024) cnt[m] = 0;
+  __syncthreads();
+  auto key = [&](int t) {
+    int hi = 0, lo = R;
+    for (int j = 0; j < k; j++) {
+      const int r = inv[t * k + j];
+      hi = max(hi, r);
+      lo = min(lo, r);
+    }
+    return (last ? hi : lo) / MB;
+  };
+  for (int t = tid; t < T; t += 1024) atomicAdd(&cnt[key(t)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int sum = 0;
+    for (int m = 0; m < NM; m++) { base[m] = sum; sum += cnt[m]; }
+  }
+  __syncthreads();
+  for (int m = tid; m <= NM; m += 1024)
+    tl_off[m] = m < NM ? base[m] : base[NM - 1] + cnt[NM - 1];
+  __syncthreads();  // the offsets are read from base before placement moves it
+  for (int t = tid; t < T; t += 1024) tl[atomicAdd(&base[key(t)], 1)] = t;
+}
+
+void launch_pipe_offsets(const int32_t *offsets, int E, int R, int MB, int NM, int32_t *moff,
+                         int32_t *mts, hipStream_t s) {
+  hipLaunchKernelGGL(pipe_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, R, MB, NM, moff,
+                     mts);
+}
+
+void launch_pipe_lists(const int32_t *inv, int T, int k, int R, int MB, int NM, bool last,
+                       int32_t *tl, int32_t *tl_off, hipStream_t s) {
+  hipLaunchKernelGGL(pipe_lists_kernel, dim3(1), dim3(1024), 0, s, inv, T, k, R, MB, NM,
+                     last ? 1 : 0, tl, tl_off);
 }
 
 // ---------------------------------------------------------------------------
