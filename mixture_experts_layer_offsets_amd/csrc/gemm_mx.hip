@@ -72,32 +72,47 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t *__rest
   if (e == 0) poff[0] = 0;
 }
 
-// Thread = (column c, 32-row block b of the padded row space): reads the
-// block's rows of column c (zeros past the expert's rows), converts them as
-// one MX block, writes 32 codes to q[c][32b ..] and the scale byte.
-__global__ __launch_bounds__(128) void quant_cols_mx_kernel(
+// Workgroup = (64 columns, one 128-row stage of the padded row space; a stage
+// never straddles two experts).  The stage's rows of the 64 columns (zeros
+// past the expert's rows) are loaded with 16-byte row-wise loads into LDS;
+// then wave q converts 32-row block q, one column per lane, reading LDS
+// row-wise (conflict-free), and writes the block's 32 codes to q[c] and its
+// scale byte -- the four waves together fill each column's 128-byte line.
+__global__ __launch_bounds__(256) void quant_cols_mx_kernel(
     const uint16_t *__restrict__ src, int C, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ poff, int E, long Rp, uint8_t *__restrict__ q,
     uint8_t *__restrict__ sc) {
-  const int c = blockIdx.x * 128 + threadIdx.x;
-  const int b = blockIdx.y, kp = b * 32;
-  if (c >= C || kp >= poff[E]) return;
+  __shared__ uint4 tile[MXK][8];  // 128 rows x 64 bf16
+  const int c0 = blockIdx.x * 64;
+  const int st = blockIdx.y, kp = st * MXK;
+  if (kp >= poff[E]) return;  // uniform over the workgroup
   int lo = 0, hi = E;  // poff[lo] <= kp < poff[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (poff[mid] <= kp) lo = mid; else hi = mid;
   }
   const int r0 = offsets[lo] + (kp - poff[lo]), rend = offsets[lo + 1];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int chunk = tid + 256 * i, row = chunk >> 3, c8 = chunk & 7;
+    const int r = r0 + row, c = c0 + 8 * c8;
+    tile[row][c8] = (r < rend && c < C) ? *(const uint4 *)(src + (size_t)r * C + c)
+                                        : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  const int blk = tid >> 6, j = tid & 63, c = c0 + j;
+  if (c >= C) return;
+  const uint16_t *t16 = (const uint16_t *)tile;
   float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; i++)
-    v[i] = r0 + i < rend ? bf16_to_f32(src[(size_t)(r0 + i) * C + c]) : 0.0f;
+  for (int i = 0; i < 32; i++) v[i] = bf16_to_f32(t16[(32 * blk + i) * 64 + j]);
   uint32_t w[8];
   const uint32_t s = mx_block32(v, w, nullptr);
-  uint4 *dst = (uint4 *)(q + (size_t)c * Rp + kp);
+  uint4 *dst = (uint4 *)(q + (size_t)c * Rp + kp + 32 * blk);
   dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  sc[((size_t)(b >> 2) * C + c) * 4 + (b & 3)] = (uint8_t)s;
+  sc[((size_t)st * C + c) * 4 + blk] = (uint8_t)s;
 }
 
 // One 256 x 256 tile of expert order[gi]'s weight gradient C_e[M][N] =
@@ -136,7 +151,7 @@ void launch_quant_cols_mx(const uint16_t *src, int R, int C, const int32_t *offs
                           hipStream_t s) {
   (void)R;
   if (C <= 0 || Rp <= 0) return;
-  hipLaunchKernelGGL(quant_cols_mx_kernel, dim3((C + 127) / 128, (unsigned)(Rp / 32)), dim3(128),
+  hipLaunchKernelGGL(quant_cols_mx_kernel, dim3((C + 63) / 64, (unsigned)(Rp / MXK)), dim3(256),
                      0, s, src, C, offsets, poff, E, Rp, q, sc);
 }
 
