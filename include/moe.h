@@ -173,7 +173,8 @@ int moe_prepare_weights(const moe_shape *shape, const uint16_t *w_gate,
 /* Router logits: logits[t][e] = fp32(sum_h x[t][h] * w_router[h][e]) +
  * bias[e] (bias may be NULL).  The router re-decides every step which
  * experts a token visits [KC §01].  x [T][H] bf16, w_router [H][E] bf16,
- * logits [T][E] fp32 (all device). */
+ * logits [T][E] fp32 (all device).  E must be a multiple of 8 (whole 16-byte
+ * rows of w_router); other E return MOE_ERR_UNSUPPORTED. */
 int moe_router_logits(const moe_shape *shape, const uint16_t *x,
                       const uint16_t *w_router, const float *bias,
                       float *logits, void *ws, size_t ws_bytes, void *stream);
@@ -236,8 +237,9 @@ int moe_combine(const moe_shape *shape, const uint16_t *y,
 /* Whole forward: [router logits, top-k] or supplied routing, layout,
  * dispatch, expert FFN (+ the shared expert), combine.
  * Routing: pass w_router (+ optional bias) with topk_idx_in = topk_w_in =
- * NULL, or pass topk_idx_in [T][k] / topk_w_in [T][k] (device) with
- * w_router = NULL.  x [T][H] bf16, out [T][H] bf16, saved (device,
+ * NULL (then k <= E, and E a multiple of 8 as for moe_router_logits), or
+ * pass topk_idx_in [T][k] / topk_w_in [T][k] (device) with
+ * w_router = NULL (any E).  x [T][H] bf16, out [T][H] bf16, saved (device,
  * moe_saved_bytes) receives the context moe_layer_bwd reads.  `sched` may
  * be NULL (defaults). */
 int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched,

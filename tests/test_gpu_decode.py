@@ -5,8 +5,9 @@ kernels (fp32 dot products summed in a different order than the MFMA
 tiles), so it is compared with the oracle at the bf16 tolerance, and with
 moe_layer_fwd on the same inputs at the same tolerance.  Cases: one token,
 a few tokens, a token count that is not a multiple of anything, experts with
-more than one 8-row pass (supplied routing with duplicates), unused experts,
-the shared expert, the Kimi-shaped dimensions, and MXFP8 shapes (refused).
+more than one 64-row pass (supplied routing with duplicates), unused experts,
+the shared expert, the Kimi-shaped dimensions, top-k above 8 (router and
+supplied routing), and MXFP8 shapes (refused).
 """
 import numpy as np
 import pytest
@@ -42,6 +43,9 @@ CASES = {
                               router_std=1 / np.sqrt(512), hot_experts=2, hot_bias=1.0, seed=5),
     "kimi-dims-t4": synth.custom(T=4, H=7168, E=6, k=8, I=2048, zipf_s=1.0,
                                  routing="supplied", seed=6),
+    "t7-k16-router": synth.custom(T=7, H=512, E=32, k=16, I=256, routing="router",
+                                  router_std=0.05, seed=14),
+    "t3-k11-supplied": synth.custom(T=3, H=256, E=5, k=11, I=128, routing="supplied", seed=15),
 }
 
 

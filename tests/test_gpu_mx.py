@@ -114,6 +114,9 @@ MX_CASES = {
     "mx-ragged": _mx(T=777, H=384, E=5, k=3, I=256),
     "mx-T1": synth.custom(T=1, H=256, E=8, k=2, I=128, routing="router", router_std=0.1,
                           mx=True, seed=2),
+    "mx-k16-router": synth.custom(T=200, H=256, E=24, k=16, I=128, routing="router",
+                                  router_std=1 / 16, mx=True, seed=12),
+    "mx-k12": _mx(T=300, H=384, E=14, k=12, I=256, zipf_s=1.0),
 }
 
 

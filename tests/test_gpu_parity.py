@@ -127,6 +127,13 @@ LAYER_CASES = {
     "E1k1": _small(T=200, H=256, E=1, k=1, I=128),
     "T1": synth.custom(T=1, H=256, E=8, k=2, I=128, routing="router", router_std=0.1, seed=2),
     "ragged": _small(T=777, H=320, E=5, k=3, I=192),
+    # top-k above 8 takes the 16-slot kernel instances (router, dispatch,
+    # combine, reverse kernels); 16 is the library's bound
+    "k16-router": synth.custom(T=300, H=256, E=32, k=16, I=128, routing="router",
+                               router_std=1 / 16, seed=11),
+    "k12-shared": _small(T=257, H=320, E=20, k=12, I=192, shared_I=128, zipf_s=1.0),
+    "k9-router": synth.custom(T=129, H=256, E=16, k=9, I=128, routing="router",
+                              router_std=1 / 16, seed=12),
 }
 
 

@@ -116,6 +116,11 @@ CASES = {
                                      hot_experts=2, hot_bias=1.0, mx=True, seed=3),
     "mx-supplied": synth.custom(T=700, H=768, E=6, k=8, I=384, zipf_s=1.2,
                                 routing="supplied", mx=True, seed=7),
+    # top-k above 8: the 16-slot token-list, combine and reverse kernels
+    "k16-router": synth.custom(T=300, H=256, E=32, k=16, I=128, routing="router",
+                               router_std=1 / 16, seed=11),
+    "mx-k12": synth.custom(T=300, H=384, E=14, k=12, I=256, zipf_s=1.0, routing="supplied",
+                           mx=True, seed=13),
 }
 
 # default; the smallest minibatch with a one-minibatch window; a minibatch
