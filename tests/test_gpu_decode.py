@@ -46,6 +46,8 @@ CASES = {
     "t7-k16-router": synth.custom(T=7, H=512, E=32, k=16, I=256, routing="router",
                                   router_std=0.05, seed=14),
     "t3-k11-supplied": synth.custom(T=3, H=256, E=5, k=11, I=128, routing="supplied", seed=15),
+    "t5-E1024-router": synth.custom(T=5, H=256, E=1024, k=8, I=64, routing="router",
+                                    router_std=0.05, seed=23),
 }
 
 

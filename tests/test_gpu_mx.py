@@ -117,6 +117,8 @@ MX_CASES = {
     "mx-k16-router": synth.custom(T=200, H=256, E=24, k=16, I=128, routing="router",
                                   router_std=1 / 16, mx=True, seed=12),
     "mx-k12": _mx(T=300, H=384, E=14, k=12, I=256, zipf_s=1.0),
+    "mx-E264-router": synth.custom(T=256, H=256, E=264, k=4, I=128, routing="router",
+                                   router_std=1 / 16, mx=True, seed=24),
 }
 
 

@@ -134,6 +134,11 @@ LAYER_CASES = {
     "k12-shared": _small(T=257, H=320, E=20, k=12, I=192, shared_I=128, zipf_s=1.0),
     "k9-router": synth.custom(T=129, H=256, E=16, k=9, I=128, routing="router",
                               router_std=1 / 16, seed=12),
+    # the library's expert bound (1024; the router's 16-slot top-k, many
+    # experts without rows) and an expert count that is not a multiple of 8
+    "E1024-router": synth.custom(T=512, H=256, E=1024, k=8, I=64, routing="router",
+                                 router_std=1 / 16, seed=21),
+    "E517-supplied": _small(T=400, H=256, E=517, k=6, I=128, zipf_s=0.8),
 }
 
 

@@ -121,6 +121,9 @@ CASES = {
                                router_std=1 / 16, seed=11),
     "mx-k12": synth.custom(T=300, H=384, E=14, k=12, I=256, zipf_s=1.0, routing="supplied",
                            mx=True, seed=13),
+    # 1024 experts, most minibatches spanning many of them
+    "E1024-router": synth.custom(T=512, H=256, E=1024, k=8, I=64, routing="router",
+                                 router_std=1 / 16, seed=21),
 }
 
 # default; the smallest minibatch with a one-minibatch window; a minibatch
