@@ -29,7 +29,7 @@
 // G2(1), ... The tiles and the combine are the same code as the staged
 // kernels, so the outputs are bit-identical to the staged forward.
 //
-// Every wait is bounded (watchdog): a wait that exceeds its poll budget sets
+// Every wait is bounded (watchdog): a wait that exceeds its real-time budget sets
 // the status word to MOE_ERR_DEVICE_TIMEOUT and the workgroup exits; the
 // others then time out too, so the kernel always finishes.
 #include "../../include/moe.h"
@@ -92,27 +92,32 @@ __device__ Task next_task(int32_t *ctr, const int32_t *ph_kind, const int32_t *p
   return t;
 }
 
-// Every thread polls *flag until it reaches `target` (uniform control flow:
-// no lane-divergent loop holds a barrier); the workgroup then agrees on the
-// outcome.  A wait that outlasts the watchdog, or any wait after another
+// Thread 0 alone polls *flag until it reaches `target`, with sleeps that
+// grow to ~2 us; the other waves wait at the barrier.  Every poll is a
+// device-coherent load that leaves the XCD, and all of them hit the one line
+// of counters that the producers' signalling atomics also need: with all 256
+// threads of ~200 waiting workgroups polling every few hundred cycles, that
+// line would see billions of requests per second, and the producers'
+// signals and rows would queue behind them.  The status word is read every
+// eighth poll.  A wait that outlasts the watchdog, or any wait after another
 // workgroup reported a timeout, fails and leaves MOE_ERR_DEVICE_TIMEOUT in
-// the status word.
+// the status word; the workgroup then agrees on the outcome.
 __device__ bool wait_all(const MkArgs &a, const int32_t *flag, int target, int *sh_fail) {
-  if (threadIdx.x == 0) *sh_fail = 0;
-  __syncthreads();
-  const unsigned long long t0 = now_ticks();
-  bool ok = true;
-  for (;;) {
-    if (ld_poll(flag) >= target) break;
-    if (ld_poll(a.status) != MOE_OK || now_ticks() - t0 > a.watchdog_ticks) {
-      ok = false;
-      break;
+  if (threadIdx.x == 0) {
+    const unsigned long long t0 = now_ticks();
+    int fail = 0, nap = 1;
+    for (int n = 0;; n++) {
+      if (ld_poll(flag) >= target) break;
+      if ((n & 7) == 7 &&
+          (ld_poll(a.status) != MOE_OK || now_ticks() - t0 > a.watchdog_ticks)) {
+        fail = 1;
+        break;
+      }
+      for (int z = 0; z < nap; z++) __builtin_amdgcn_s_sleep(16);  // ~1000 cycles each
+      nap = min(2 * nap, 4);
     }
-    __builtin_amdgcn_s_sleep(8);
-  }
-  if (!ok) {
-    atomicCAS(a.status, MOE_OK, MOE_ERR_DEVICE_TIMEOUT);
-    *sh_fail = 1;  // any thread may set it
+    if (fail) atomicCAS(a.status, MOE_OK, MOE_ERR_DEVICE_TIMEOUT);
+    *sh_fail = fail;
   }
   __syncthreads();
   const bool all_ok = *sh_fail == 0;
