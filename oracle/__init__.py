@@ -15,11 +15,13 @@ Modules:
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 something other than itself (hand-computed fixtures, closed forms, library
 routines, brute force, finite differences, an independent autograd
-formulation), except the MX recipe of the backward pass, which is a
-self-consistent definition ("parity unpinned" for that recipe choice; its
-arithmetic is still pinned through the quantiser and the bf16 path).
+formulation, weights exactly representable along one axis only for the MX
+quantisation axes), except the choice of the MX recipe of the backward pass
+(which tensors the backward quantises): "parity unpinned" for that choice,
+since the pages do not say; its arithmetic is pinned through the quantiser,
+the weight axes and the bf16 path.
 """
 from . import layer, mx, numerics  # noqa: F401
-from .layer import (TokenEvaluator, backward, combine, dispatch,  # noqa: F401
-                    expert_weight_grad_columns, forward, layout, router_backward,
-                    router_logits, topk_softmax)
+from .layer import (ExpertWeights, TokenEvaluator, backward, combine,  # noqa: F401
+                    dispatch, expert_weight_grad_columns, forward, layout,
+                    router_backward, router_logits, topk_softmax)

@@ -23,6 +23,9 @@ layout), Dispatch, Expert FFN, Combine and the final weighted fusion.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .mx import mx_quantize, mx_roundtrip, mx_rows_roundtrip
@@ -147,11 +150,11 @@ def _swiglu_rows(Xhat, Wg, Wu, Wd, mx, R):
 
     SwiGLU is named as the expert activation [KC §02]; reading: the gate
     projection goes through silu, multiplies the up projection, and the down
-    projection follows, with no biases.  g and u are held in fp32 and a is
-    formed in fp32 (the GEMM accumulator's precision), so the bf16 rounding or
-    MX quantisation of a decides from an fp32 value as the kernel does; a is
-    stored as bf16, or with MXFP8 quantised along the intermediate axis (the
-    SwiGLU epilogue quantises [KC §02]); Y is stored as bf16.
+    projection follows, with no biases.  The layer's precision is bf16
+    storage with fp32 accumulation, so g and u are fp32 values and a, an
+    elementwise function of them, is formed at that same precision before it
+    is stored: as bf16, or with MXFP8 quantised along the intermediate axis
+    (the SwiGLU path quantises [KC §02]).  Y is stored as bf16.
     """
     g = R.f32(Xhat @ Wg)
     u = R.f32(Xhat @ Wu)
@@ -161,52 +164,94 @@ def _swiglu_rows(Xhat, Wg, Wu, Wd, mx, R):
     return g, u, ahat, Y
 
 
-def _weights(inp, mx):
-    """Expert weights as the forward and the backward GEMMs see them.
+def expert_weights(w_gate, w_up, w_down, mx, backward=False):
+    """One expert's weights as one direction's GEMMs see them.
 
     With MXFP8 every GEMM operand is quantised along that GEMM's contraction
-    axis: the forward gate/up along H and down along I; the backward data
-    gradients use copies of gate/up quantised along I and of down along H.
+    axis.  The forward contracts gate/up ([H, I]) over H and down ([I, H])
+    over I: axis -2 of each.  The backward data gradients contract gate/up
+    over I (dX = dg W_gate^T) and down over H (dA = dY W_down^T): axis -1.
+    Returns dict(g, u, d) in fp64.
     """
-    Wg, Wu, Wd = _val(inp["w_gate"]), _val(inp["w_up"]), _val(inp["w_down"])
+    Wg, Wu, Wd = _val(w_gate), _val(w_up), _val(w_down)
     if not mx:
-        return dict(g=Wg, u=Wu, d=Wd, g_b=Wg, u_b=Wu, d_b=Wd)
-    return dict(g=mx_roundtrip(Wg, axis=-2), u=mx_roundtrip(Wu, axis=-2),
-                d=mx_roundtrip(Wd, axis=-2),
-                g_b=mx_roundtrip(Wg, axis=-1), u_b=mx_roundtrip(Wu, axis=-1),
-                d_b=mx_roundtrip(Wd, axis=-1))
+        return dict(g=Wg, u=Wu, d=Wd)
+    ax = -1 if backward else -2
+    return dict(g=mx_roundtrip(Wg, axis=ax), u=mx_roundtrip(Wu, axis=ax),
+                d=mx_roundtrip(Wd, axis=ax))
 
 
-def _shared_weights(inp, mx):
-    if inp.get("ws_gate") is None:
-        return None
-    return _weights(dict(w_gate=inp["ws_gate"], w_up=inp["ws_up"],
-                         w_down=inp["ws_down"]), mx)
+class ExpertWeights:
+    """The routed (or shared) experts' weights, decoded one expert at a time
+    on request: a 256-expert layer's decoded weights would not fit in host
+    memory at once.  ``fwd(e)`` / ``bwd(e)`` give dict(g, u, d) as the
+    forward / backward data-gradient GEMMs see them."""
+
+    def __init__(self, inp, mx, shared=False):
+        if shared:
+            self.src = (inp["ws_gate"][None], inp["ws_up"][None], inp["ws_down"][None])
+        else:
+            self.src = (inp["w_gate"], inp["w_up"], inp["w_down"])
+        self.mx = mx
+        self.E = self.src[0].shape[0]
+
+    def fwd(self, e):
+        return expert_weights(self.src[0][e], self.src[1][e], self.src[2][e], self.mx)
+
+    def bwd(self, e):
+        return expert_weights(self.src[0][e], self.src[1][e], self.src[2][e], self.mx,
+                              backward=True)
+
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def _each(fn, items):
+    """fn(item) for every item, on a pool of THREADS threads (numpy's large
+    array operations release the interpreter lock).  Every call writes only
+    its own expert's rows or gradients, so the results do not depend on the
+    order the calls run in."""
+    items = list(items)
+    if THREADS <= 1 or len(items) <= 1:
+        for it in items:
+            fn(it)
+        return
+    with ThreadPoolExecutor(min(THREADS, len(items))) as ex:
+        list(ex.map(fn, items))
 
 
 # ----------------------------------------------------------------------------
 # Whole layer
 
 
-def forward(inp, k, mx=False, exact=False, routing=None):
+def forward(inp, k, mx=False, exact=False, routing=None, logits=None):
     """The layer's forward pass; returns every intermediate the backward needs.
 
     ``inp`` holds x, the expert weights and either a router (w_router, bias)
     or supplied routing (topk_idx, topk_w); the optional shared expert
     (ws_gate, ws_up, ws_down) runs densely on every token with weight one.
-    ``routing`` (idx, w) overrides the router (used by the exact-mode
-    gradient tests, where selection must stay fixed).
+    ``logits`` (fp32 [T, E]) replaces the router's logits as the input of the
+    selection and the weights: the selection is defined given the fp32
+    logits, so a check of another implementation's routing passes that
+    implementation's logits here (the router backward still runs).
+    ``routing`` (idx, w) overrides the router altogether (used by the
+    exact-mode gradient tests, where the selection must stay fixed).
     """
     if exact and mx:
         raise ValueError("exact mode has no quantiser")
     R = _Round(exact)
     x = _val(inp["x"])
     T, H = x.shape
-    W = _weights(inp, mx)
-    E, _, I = W["g"].shape
-    logits = None
+    W = ExpertWeights(inp, mx)
+    E = W.E
+    I = inp["w_gate"].shape[2]
     if routing is not None:
         idx, w = np.asarray(routing[0], np.int32), np.asarray(routing[1], np.float64)
+    elif logits is not None:
+        logits = np.asarray(logits, np.float64)
+        if logits.shape != (T, E) or not np.array_equal(logits, f32(logits)):
+            raise ValueError("forward: logits must be fp32 values of shape [T, E]")
+        idx, w = topk_softmax(logits, k, exact)
     elif inp.get("topk_idx") is None:
         logits = router_logits(x, inp["w_router"], inp.get("bias"), exact)
         idx, w = topk_softmax(logits, k, exact)
@@ -220,15 +265,17 @@ def forward(inp, k, mx=False, exact=False, routing=None):
     Rn = T * k
     g = np.zeros((Rn, I)); u = np.zeros((Rn, I))
     ahat = np.zeros((Rn, I)); Y = np.zeros((Rn, H))
-    for e in range(E):
+
+    def one(e):
         rs = slice(int(offsets[e]), int(offsets[e + 1]))
-        if rs.stop > rs.start:
-            g[rs], u[rs], ahat[rs], Y[rs] = _swiglu_rows(
-                Xhat[rs], W["g"][e], W["u"][e], W["d"][e], mx, R)
-    WS = _shared_weights(inp, mx)
+        We = W.fwd(e)
+        g[rs], u[rs], ahat[rs], Y[rs] = _swiglu_rows(Xhat[rs], We["g"], We["u"], We["d"], mx, R)
+    _each(one, [e for e in range(E) if counts[e]])
+    WS = ExpertWeights(inp, mx, shared=True) if inp.get("ws_gate") is not None else None
     shared = None
     if WS is not None:
-        gs, us, as_, ys = _swiglu_rows(xhat_tok, WS["g"], WS["u"], WS["d"], mx, R)
+        Ws = WS.fwd(0)
+        gs, us, as_, ys = _swiglu_rows(xhat_tok, Ws["g"], Ws["u"], Ws["d"], mx, R)
         shared = dict(g=gs, u=us, ahat=as_, y=ys)
     out = combine(Y, w, inv, k, None if shared is None else shared["y"], exact)
     return dict(k=k, mx=mx, exact=exact, x=x, xhat_tok=xhat_tok, logits=logits,
@@ -259,6 +306,9 @@ def combine(Y, w, inv, k, y_shared=None, exact=False):
 def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R, mx_wgrad=False):
     """Backward of one expert's SwiGLU FFN given its rows' output gradient dY.
 
+    ``Wb`` holds the expert's weights as the backward data-gradient GEMMs see
+    them (:meth:`ExpertWeights.bwd`).
+
     dA = dY' Wd^T; dg = dA u silu'(g); du = dA silu(g) (stored as bf16);
     dWd = ahat^T dY; dWg = Xhat^T dg; dWu = Xhat^T du (fp32);
     dX = dg' Wg^T + du' Wu^T (bf16).  With MXFP8 the data-gradient GEMM
@@ -270,7 +320,7 @@ def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R, mx_wgrad=False):
     silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
     """
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
-    dA = R.f32(dYq @ Wb["d_b"].T)
+    dA = R.f32(dYq @ Wb["d"].T)
     s = sigmoid(g)
     dg = R.bf16(dA * u * s * (1.0 + g * (1.0 - s)))
     du = R.bf16(dA * g * s)
@@ -284,7 +334,7 @@ def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R, mx_wgrad=False):
     dWu = R.f32(Xw.T @ duw)
     dgq = mx_roundtrip(dg, axis=1) if mx else dg
     duq = mx_roundtrip(du, axis=1) if mx else du
-    dX = R.bf16(dgq @ Wb["g_b"].T + duq @ Wb["u_b"].T)
+    dX = R.bf16(dgq @ Wb["g"].T + duq @ Wb["u"].T)
     return dict(dA=dA, dg=dg, du=du, dWd=dWd, dWg=dWg, dWu=dWu, dX=dX)
 
 
@@ -319,15 +369,15 @@ def backward(inp, fw, dout=None, mx_wgrad=False):
     dg = np.zeros((Rn, I)); du = np.zeros((Rn, I)); dX = np.zeros((Rn, H))
     dWg = np.zeros((E, H, I)); dWu = np.zeros((E, H, I)); dWd = np.zeros((E, I, H))
     W = fw["W"]
-    for e in range(E):
+    counts = np.diff(offsets)
+
+    def one(e):
         rs = slice(int(offsets[e]), int(offsets[e + 1]))
-        if rs.stop == rs.start:
-            continue
-        Wb = dict(d_b=W["d_b"][e], g_b=W["g_b"][e], u_b=W["u_b"][e])
         b = _swiglu_rows_bwd(fw["Xhat"][rs], fw["g"][rs], fw["u"][rs], fw["ahat"][rs],
-                             dY[rs], Wb, mx, R, mx_wgrad)
+                             dY[rs], W.bwd(e), mx, R, mx_wgrad)
         dg[rs], du[rs], dX[rs] = b["dg"], b["du"], b["dX"]
         dWg[e], dWu[e], dWd[e] = b["dWg"], b["dWu"], b["dWd"]
+    _each(one, [e for e in range(E) if counts[e]])
     out = dict(dY=dY, dw=dw, dg=dg, du=du, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd)
     acc = np.zeros((T, H))
     for j in range(k):
@@ -339,9 +389,8 @@ def backward(inp, fw, dout=None, mx_wgrad=False):
         acc += dxr
     if fw["shared"] is not None:
         sh = fw["shared"]
-        WS = fw["WS"]
         b = _swiglu_rows_bwd(fw["xhat_tok"], sh["g"], sh["u"], sh["ahat"], dout,
-                             dict(d_b=WS["d_b"], g_b=WS["g_b"], u_b=WS["u_b"]), mx, R, mx_wgrad)
+                             fw["WS"].bwd(0), mx, R, mx_wgrad)
         out.update(dWsg=b["dWg"], dWsu=b["dWu"], dWsd=b["dWd"], dXs=b["dX"])
         acc += b["dX"]
     out["dx"] = R.bf16(acc)
@@ -373,30 +422,26 @@ def router_backward(x, w_router, idx, w, dw, E, exact=False):
 
 
 class _LazyWeights:
-    """Per-expert decoded weights (as the forward / backward GEMMs see them),
-    decoded on first use: the sampled evaluators touch only a few experts."""
+    """Per-expert weights of both directions, dict(fwd=..., bwd=...) as
+    :class:`ExpertWeights` gives them, decoded on first use and kept for the
+    ``keep`` most recently used experts: the sampled evaluators touch only a
+    few experts."""
 
     def __init__(self, inp, mx, shared=False, keep=16):
-        if shared:
-            self.src = (inp["ws_gate"][None], inp["ws_up"][None], inp["ws_down"][None])
-        else:
-            self.src = (inp["w_gate"], inp["w_up"], inp["w_down"])
-        self.mx = mx
+        self.src = ExpertWeights(inp, mx, shared)
         self.keep = keep
         self.cache = {}
+
+    def _decode(self, e):
+        return dict(fwd=self.src.fwd(e), bwd=self.src.bwd(e))
 
     def prefetch(self, experts, threads=8):
         """Decode several experts at once (numpy releases the GIL in the
         elementwise work, so threads overlap); the cache grows to hold them."""
-        from concurrent.futures import ThreadPoolExecutor
         todo = [int(e) for e in dict.fromkeys(experts) if int(e) not in self.cache]
         self.keep = max(self.keep, len(self.cache) + len(todo))
-
-        def one(e):
-            return _weights(dict(w_gate=self.src[0][e], w_up=self.src[1][e],
-                                 w_down=self.src[2][e]), self.mx)
         with ThreadPoolExecutor(max(1, threads)) as ex:
-            for e, We in zip(todo, ex.map(one, todo)):
+            for e, We in zip(todo, ex.map(self._decode, todo)):
                 self.cache[e] = We
 
     def __getitem__(self, e):
@@ -405,8 +450,7 @@ class _LazyWeights:
         else:
             if len(self.cache) >= self.keep:
                 self.cache.pop(next(iter(self.cache)))
-            one = dict(w_gate=self.src[0][e], w_up=self.src[1][e], w_down=self.src[2][e])
-            self.cache[e] = _weights(one, self.mx)
+            self.cache[e] = self._decode(e)
         return self.cache[e]
 
 
@@ -451,13 +495,14 @@ class TokenEvaluator:
         acc = np.zeros(self.x.shape[1])
         for j in range(self.k):
             e = int(idx[j])
-            We = self.W[e]
+            We = self.W[e]["fwd"]
             g, u, ah, Y = _swiglu_rows(xh, We["g"], We["u"], We["d"], self.mx, self.R)
             slots.append(dict(e=e, g=g, u=u, ahat=ah, Y=Y[0]))
             acc += w[j] * Y[0]
         ys = None
         if self.WS is not None:
-            ys = _swiglu_rows(xh, self.WS["g"], self.WS["u"], self.WS["d"], self.mx, self.R)
+            Ws = self.WS["fwd"]
+            ys = _swiglu_rows(xh, Ws["g"], Ws["u"], Ws["d"], self.mx, self.R)
             acc += ys[3][0]
         return dict(idx=idx, w=w, slots=slots, shared=ys, xhat=xh, out=self.R.bf16(acc))
 
@@ -469,7 +514,7 @@ class TokenEvaluator:
         dw = self.R.f32(np.array([dout_t @ s["Y"] for s in fw["slots"]]))
         acc = np.zeros_like(dout_t)
         for j, s in enumerate(fw["slots"]):
-            We = self.W[s["e"]]
+            We = self.W[s["e"]]["bwd"]
             dY = self.R.bf16(w[j] * dout_t)[None, :]
             b = _swiglu_rows_bwd(fw["xhat"], s["g"], s["u"], s["ahat"], dY, We, self.mx, self.R)
             acc += b["dX"][0]
@@ -480,22 +525,24 @@ class TokenEvaluator:
             acc += dxr[0]
         if fw["shared"] is not None:
             gs, us, as_, _ = fw["shared"]
-            b = _swiglu_rows_bwd(fw["xhat"], gs, us, as_, dout_t[None, :], self.WS, self.mx,
-                                 self.R)
+            b = _swiglu_rows_bwd(fw["xhat"], gs, us, as_, dout_t[None, :], self.WS["bwd"],
+                                 self.mx, self.R)
             acc += b["dX"][0]
         return dict(dw=dw, dx=self.R.bf16(acc))
 
 
-def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, weights=None):
+def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, weights=None,
+                               logits=None):
     """dW_down[e, i, :], dW_gate[e, :, i], dW_up[e, :, i] for chosen columns i.
 
     Sums over the rows routed to expert e (found from the routing by
     :func:`layout`), recomputing only the 32-column blocks of g, u, a and dA
     that the chosen columns fall in.  For sampled checks at full size.
-    Router routing is evaluated in full (it is cheap); the FFN is not.
+    Router routing is evaluated in full (it is cheap), from ``logits`` when
+    given (as :func:`forward` takes them); the FFN is not.
     With ``shared`` the expert is the shared one: every token, weight one.
-    ``weights`` may pass the decoded weights of the expert (as a
-    TokenEvaluator holds them) to skip decoding them again.
+    ``weights`` may pass the expert's decoded weights, dict(fwd=..., bwd=...)
+    (as a TokenEvaluator holds them), to skip decoding them again.
     """
     R = _Round(False)
     x = _val(inp["x"])
@@ -506,7 +553,9 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, wei
         wrow = np.ones(x.shape[0])
     else:
         We = weights if weights is not None else _LazyWeights(inp, mx)[e]
-        if inp.get("topk_idx") is None:
+        if logits is not None:
+            idx, w = topk_softmax(logits, k)
+        elif inp.get("topk_idx") is None:
             L = router_logits(x, inp["w_router"], inp.get("bias"))
             idx, w = topk_softmax(L, k)
         else:
@@ -516,17 +565,18 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, wei
         f = perm[offsets[e]:offsets[e + 1]].astype(np.int64)
         t = f // k
         wrow = np.asarray(w, np.float64).reshape(-1)[f]
+    Wf, Wb = We["fwd"], We["bwd"]
     xh = mx_roundtrip(x[t], axis=1) if mx else x[t]
     dY = R.bf16(wrow[:, None] * dout[t])
     cols = np.asarray(cols)
     blocks = np.unique(cols // 32)
     bc = np.concatenate([np.arange(b * 32, b * 32 + 32) for b in blocks])
-    g = R.f32(xh @ We["g"][:, bc])
-    u = R.f32(xh @ We["u"][:, bc])
+    g = R.f32(xh @ Wf["g"][:, bc])
+    u = R.f32(xh @ Wf["u"][:, bc])
     a = R.f32(silu(g) * u)
     ah = mx_roundtrip(a, axis=1) if mx else R.bf16(a)
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
-    dA = R.f32(dYq @ We["d_b"][bc, :].T)
+    dA = R.f32(dYq @ Wb["d"][bc, :].T)
     s = sigmoid(g)
     dg = R.bf16(dA * u * s * (1.0 + g * (1.0 - s)))
     du = R.bf16(dA * g * s)

@@ -31,30 +31,32 @@ BLOCK = 32
 
 
 def e4m3_encode(v) -> np.ndarray:
-    """Encode values with |v| <= 448 to E4M3 codes (uint8), nearest-even."""
+    """Encode values with |v| <= 448 to E4M3 codes (uint8), nearest-even.
+
+    A value in the binade [2^e, 2^(e+1)) (e >= -6) is a multiple of the
+    quantum 2^(e-3); below the smallest normal 2^-6 the quantum stays the
+    subnormal one, 2^-9, so the binade exponent is floored at -6.  With
+    q = |v| / 2^(e-3) rounded to the nearest integer (ties to even), q lies
+    in [8, 16] for a normal and in [0, 8] below the normals, and the code's
+    low seven bits are 8 (e + 6) + q: exponent field e + 7 with mantissa
+    q - 8 for a normal, the subnormal mantissa q itself when e = -6, and a
+    q of 16 (or of 8 from below the normals) is the next binade's
+    mantissa 0.
+    """
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
     if np.any(a > E4M3_MAX) or np.any(np.isnan(a)):
         raise ValueError("e4m3_encode: value outside [-448, 448]")
-    code = np.zeros(v.shape, dtype=np.int64)
-    sub = a < 2.0 ** -6
-    # Below the smallest normal the spacing is 2^-9; q = 8 lands exactly on
-    # 2^-6, whose code (exponent field 1, mantissa 0) is also 8.
-    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)
-    nrm = ~sub
-    _, ex = np.frexp(a[nrm])          # a = m * 2^ex with m in [0.5, 1)
-    e = ex.astype(np.int64) - 1       # a in [2^e, 2^(e+1))
-    q = np.rint(np.ldexp(a[nrm], 3 - e)).astype(np.int64)  # in [8, 16]
-    up = q == 16
-    q[up] = 8
-    e[up] += 1
-    code[nrm] = ((e + 7) << 3) | (q - 8)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -7))   # a = m 2^ex with m in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    q = np.rint(np.ldexp(a, 3 - e)).astype(np.int64)
+    code = 8 * (e + 6) + q
     code |= (v < 0).astype(np.int64) << 7
     return code.astype(np.uint8)
 
 
-def e4m3_decode(code) -> np.ndarray:
-    """Value of E4M3 codes (fp64); the NaN codes decode to NaN."""
+def _e4m3_value(code) -> np.ndarray:
+    """Value of E4M3 codes from their bit fields (fp64); NaN codes give NaN."""
     c = np.asarray(code, dtype=np.uint8).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     ex = (c >> 3) & 0xF
@@ -63,6 +65,15 @@ def e4m3_decode(code) -> np.ndarray:
                    np.ldexp((8 + man).astype(np.float64), ex - 10))
     mag = np.where((ex == 15) & (man == 7), np.nan, mag)
     return sign * mag
+
+
+_E4M3_VALUES = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of E4M3 codes (fp64): a lookup in the table of all 256 codes
+    built from the bit fields; the NaN codes decode to NaN."""
+    return _E4M3_VALUES[np.asarray(code, dtype=np.uint8)]
 
 
 def e8m0_decode(code) -> np.ndarray:

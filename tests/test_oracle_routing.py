@@ -120,3 +120,25 @@ def test_dsv3_hot_expert_share():
     share = np.isin(idx, inp["hot"]).mean()
     assert math.ceil(0.1 * w.E) == w.hot_experts == len(inp["hot"])
     assert 0.49 <= share <= 0.51, share
+
+
+def test_forward_routes_from_given_logits():
+    """forward(logits=L) with the router's own fp32 logits reproduces the
+    router-routed layer bit for bit (backward included); other logits change
+    the selection exactly as topk_softmax of them does."""
+    import oracle
+    w = synth.custom(T=40, H=64, E=8, k=3, I=32, routing="router", router_std=0.3, seed=4)
+    inp = synth.make_inputs(w)
+    a = oracle.forward(inp, w.k)
+    b = oracle.forward(inp, w.k, logits=a["logits"])
+    for key in ("idx", "w", "perm", "out", "Y"):
+        assert np.array_equal(a[key], b[key]), key
+    ga, gb = oracle.backward(inp, a), oracle.backward(inp, b)
+    for key in ("dx", "dWr", "dWg", "dw"):
+        assert np.array_equal(ga[key], gb[key]), key
+    L2 = a["logits"][:, ::-1].copy()
+    c = oracle.forward(inp, w.k, logits=L2)
+    idx, wts = oracle.topk_softmax(L2, w.k)
+    assert np.array_equal(c["idx"], idx) and np.array_equal(c["w"], wts)
+    with np.testing.assert_raises(ValueError):
+        oracle.forward(inp, w.k, logits=a["logits"] + 1e-12)
