@@ -6,8 +6,8 @@
  *   [KC] kucoin.com news flash "O MoK do Cursor alcança aumento de desempenho
  *        de 2,37x no NVIDIA GB300 NVL72", §01 "O imposto sobre comunicações
  *        do MoE", §02 (pull dispatch, megakernel, ring buffer), §03
- *        (benchmark: "Schedule, Dispatch, Expert FFN, Combine e a fusão
- *        ponderada final").
+ *        (benchmark of the whole layer: scheduling, dispatch, the experts'
+ *        FFN, combine and the weighted sum that ends it).
  *   [NA] noticiai.com.br "Cursor abre código do Mixture-of-Kittens: kernel
  *        MoE que acelera treinamento em GPUs Blackwell em até 2,37×",
  *        section "As três decisões de design que fazem a diferença".
@@ -36,7 +36,8 @@
  *   outputs, run to run (no floating-point atomics; every reduction has a
  *   fixed order).
  * - No token is dropped and no buffer depends on the routing: every (t, j)
- *   owns one row ([NA] "Buffer em anel elimina a CPU do loop").
+ *   owns one row (the pages' ring buffer exists so that neither tokens are
+ *   dropped nor the CPU sizes buffers per step [NA design, item 3]).
  * - Errors: each int-returning call returns MOE_OK or one of the codes
  *   below and enqueues nothing when it fails its argument checks.
  */
@@ -93,11 +94,16 @@ typedef struct moe_shape {
  *   the minibatches in reverse [NA design].  With comm_cus > 0 the
  *   communication stream is limited to comm_cus CUs and the GEMM streams to
  *   the rest (hardware CU masks); with comm_cus = 0 all three share every CU.
- *   The streams and events are the library's own, created on the first
- *   pipelined call on each device and kept until the process ends; pipelined
- *   calls on one device are enqueued one at a time (a mutex) and run on the
- *   same streams, so they execute in call order.  Outputs are bit-identical
- *   to MOE_SCHED_STAGED. */
+ *   The streams and events are the library's own: one set of three streams
+ *   per comm_cus value, created on the first pipelined call with that value
+ *   on each device and kept until the process ends, so no call waits for
+ *   earlier work; at most 8 distinct comm_cus values per device (a ninth is
+ *   refused with MOE_ERR_UNSUPPORTED, and comm_cus >= the device's CU count
+ *   with MOE_ERR_INVALID_ARG, before anything is enqueued).  Pipelined calls
+ *   on one device are enqueued one at a time (a mutex); every call forks
+ *   from and joins back to the caller's stream, so calls on one caller
+ *   stream execute in call order.  Outputs are bit-identical to
+ *   MOE_SCHED_STAGED. */
 enum { MOE_SCHED_STAGED = 0, MOE_SCHED_PERSISTENT = 1, MOE_SCHED_PIPELINED = 2 };
 
 /* Schedule knobs of the layer call.  The pages retune the minibatch and the
@@ -139,6 +145,14 @@ typedef struct moe_sched {
                              rows starting at each expert's first row, the
                              last block zero-padded; 0 (default) = bf16
                              weight gradients on the MX round trips */
+  void (*stage_hook)(void *user, int32_t stage);
+                          /* optional, with stage_events: called on the
+                             calling thread while the layer call enqueues,
+                             just before boundary `stage` (< n_stage_events)
+                             is recorded, so a caller can enqueue work of
+                             its own on `stream` ahead of that stage (a
+                             benchmark's cache flush); NULL = none */
+  void *stage_hook_user;  /* passed to stage_hook */
 } moe_sched;
 
 /* ------------------------------------------------------------------ sizes */
@@ -234,8 +248,10 @@ int moe_combine(const moe_shape *shape, const uint16_t *y,
 
 /* ------------------------------------------------------------- the layer */
 
-/* Whole forward: [router logits, top-k] or supplied routing, layout,
- * dispatch, expert FFN (+ the shared expert), combine.
+/* Whole forward, the layer the pages measure end to end [KC §03]:
+ * scheduling ([router logits, top-k] or supplied routing, then layout),
+ * dispatch, the expert FFN (+ the shared expert), combine and the final
+ * weighted sum.
  * Routing: pass w_router (+ optional bias) with topk_idx_in = topk_w_in =
  * NULL (then k <= E, and E a multiple of 8 as for moe_router_logits), or
  * pass topk_idx_in [T][k] / topk_w_in [T][k] (device) with
@@ -316,13 +332,21 @@ int moe_saved_pointers(const moe_shape *shape, void *saved,
                        moe_saved_view *view);
 
 /* Device pointers into a workspace (host call, no device work): where the
- * last moe_layer_bwd that used `ws` left its row intermediates, for callers
- * that inspect them (valid until the next call that uses `ws`).  Fields
- * are NULL when the shape is invalid. */
+ * last call that used `ws` left its intermediates, for callers that inspect
+ * them (valid until the next call that uses `ws`).  Fields are NULL when
+ * the shape is invalid. */
 typedef struct moe_work_view {
-  uint16_t *dy;       /* bf16 [R][H]: rows' output gradient (reverse-combine) */
-  uint16_t *dh;       /* bf16 [R][2I]: dg and du, interleaved in 32-column blocks */
-  uint16_t *dx_rows;  /* bf16 [R][H]: rows' input gradient (before reverse-dispatch) */
+  uint16_t *dy;       /* moe_layer_bwd: bf16 [R][H], rows' output gradient
+                         (reverse-combine) */
+  uint16_t *dh;       /* moe_layer_bwd: bf16 [R][2I], dg and du interleaved in
+                         32-column blocks */
+  uint16_t *dx_rows;  /* moe_layer_bwd: bf16 [R][H], rows' input gradient
+                         (before reverse-dispatch) */
+  float *dec_logits;  /* moe_decode_fwd with a router: fp32 [T][E] logits */
+  int32_t *dec_topk_idx; /* moe_decode_fwd with a router: [T][k] selection */
+  float *dec_topk_w;  /* moe_decode_fwd with a router: fp32 [T][k] weights
+                         (with supplied routing the decode reads the caller's
+                         arrays in place and writes none of these three) */
 } moe_work_view;
 
 int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view);

@@ -38,11 +38,15 @@ class MoeShape(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+STAGE_HOOK = ctypes.CFUNCTYPE(None, c_void_p, ctypes.c_int32)
+
+
 class MoeSched(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
                 ("comm_cus", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(c_void_p)), ("n_stage_events", ctypes.c_int32),
-                ("watchdog_us", ctypes.c_int32), ("mx_wgrad", ctypes.c_int32)]
+                ("watchdog_us", ctypes.c_int32), ("mx_wgrad", ctypes.c_int32),
+                ("stage_hook", STAGE_HOOK), ("stage_hook_user", c_void_p)]
 
 
 class MoeSavedView(ctypes.Structure):
@@ -228,7 +232,8 @@ def moe_saved_pointers(shape, saved) -> dict:
 
 
 class MoeWorkView(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in ("dy", "dh", "dx_rows")]
+    _fields_ = [(n, c_void_p) for n in ("dy", "dh", "dx_rows", "dec_logits", "dec_topk_idx",
+                                        "dec_topk_w")]
 
 
 def moe_workspace_pointers(shape, ws) -> dict:

@@ -2,10 +2,11 @@
 // order of kernel launches for each entry point.  No entry point allocates
 // device memory or waits for the device (moe_read_status aside).
 //
-// The layer follows the parts the pages measure -- "Schedule, Dispatch,
-// Expert FFN, Combine e a fusão ponderada final" (kucoin.com news flash "O MoK
+// The layer follows the parts the pages measure (kucoin.com news flash "O MoK
 // do Cursor alcança aumento de desempenho de 2,37x no NVIDIA GB300 NVL72",
-// §03) -- and its backward mirrors the forward's data movement (§01, §02).
+// §03): scheduling, dispatch, the experts' FFN, combine and the weighted sum
+// that ends the layer; its backward mirrors the forward's data movement (§01,
+// §02).
 // With MXFP8 the activations entering each GEMM are E4M3 codes with E8M0
 // scales (quantised in dispatch and in the SwiGLU epilogue, §02), the weights
 // are pre-quantised along each GEMM's contraction axis, and the weight
@@ -277,12 +278,15 @@ int hip_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP
 
 hipStream_t S(void *s) { return (hipStream_t)s; }
 
-// Records the caller's stage event i (if any) on the stream.
+// Stage boundary i: the caller's hook (if any), then its stage event i (if
+// any) recorded on the stream.
 struct Stages {
   const moe_sched *sc;
   hipStream_t s;
   void mark(int i) const {
-    if (sc && sc->stage_events && i < sc->n_stage_events && sc->stage_events[i])
+    if (!sc || i >= sc->n_stage_events) return;
+    if (sc->stage_hook) sc->stage_hook(sc->stage_hook_user, i);
+    if (sc->stage_events && sc->stage_events[i])
       hipEventRecord((hipEvent_t)sc->stage_events[i], s);
   }
 };
@@ -597,65 +601,98 @@ int mk_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Save
 
 static_assert(kPipeMaxMinibatches == kMkMaxMinibatches, "plan sized for the same minibatch bound");
 
-struct PipeRes {
-  bool init = false;
+// One set of streams: a communication stream and two GEMM streams, with the
+// CU masks of one comm_cus value (a CU mask is fixed when a stream is
+// created).
+struct PipeStreams {
   int comm_cus = -1;
   hipStream_t comm = nullptr, gemm[2] = {nullptr, nullptr};
+};
+
+// Distinct comm_cus values whose stream sets one device keeps; a call with
+// a further value is refused (MOE_ERR_UNSUPPORTED) rather than replacing a
+// set, which would have to wait for that set's work first.
+constexpr int kMaxStreamSets = 8;
+
+struct PipeDev {
+  PipeStreams sets[kMaxStreamSets];
+  int n_sets = 0;
   std::vector<hipEvent_t> ev;
 };
 
-std::mutex g_pipe_mu;
-PipeRes g_pipe[64];
+struct PipeRes {
+  hipStream_t comm = nullptr, gemm[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> *ev = nullptr;
+};
 
-// Streams for this comm_cus on the current device (recreated when it
-// changes: a CU mask is fixed when a stream is created), and at least
-// n_events events.  Called with g_pipe_mu held.
-int pipe_resources(int comm_cus, size_t n_events, PipeRes **out) {
+std::mutex g_pipe_mu;
+PipeDev g_pipe[64];
+
+// Creates the three streams of one comm_cus value; on failure destroys
+// whatever it created.
+int create_stream_set(int comm_cus, PipeStreams *out) {
+  const int cus = device_cus();
+  PipeStreams r;
+  r.comm_cus = comm_cus;
+  bool ok = true;
+  if (comm_cus > 0) {
+    if (comm_cus >= cus) return MOE_ERR_INVALID_ARG;
+    // CU mask bits: the first comm_cus bits of the mask go to the
+    // communication stream, the rest to the GEMM streams
+    std::vector<uint32_t> cm((cus + 31) / 32, 0u), gm((cus + 31) / 32, 0u);
+    for (int i = 0; i < cus; i++) (i < comm_cus ? cm : gm)[i / 32] |= 1u << (i % 32);
+    ok = hipExtStreamCreateWithCUMask(&r.comm, (uint32_t)cm.size(), cm.data()) == hipSuccess &&
+         hipExtStreamCreateWithCUMask(&r.gemm[0], (uint32_t)gm.size(), gm.data()) ==
+             hipSuccess &&
+         hipExtStreamCreateWithCUMask(&r.gemm[1], (uint32_t)gm.size(), gm.data()) == hipSuccess;
+  } else {
+    for (hipStream_t *q : {&r.comm, &r.gemm[0], &r.gemm[1]})
+      ok = ok && hipStreamCreateWithFlags(q, hipStreamNonBlocking) == hipSuccess;
+  }
+  if (!ok) {
+    for (hipStream_t q : {r.comm, r.gemm[0], r.gemm[1]})
+      if (q) hipStreamDestroy(q);
+    return MOE_ERR_HIP;
+  }
+  *out = r;
+  return MOE_OK;
+}
+
+// The streams of this comm_cus on the current device (created on its first
+// use and kept until the process ends, so no call ever waits for earlier
+// work to drain), and at least n_events events.  Called with g_pipe_mu held.
+int pipe_resources(int comm_cus, size_t n_events, PipeRes *out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
-  PipeRes &r = g_pipe[dev];
-  if (!r.init || r.comm_cus != comm_cus) {
-    if (r.init) {
-      // streams of an earlier comm_cus: let their work finish, then drop them
-      for (hipStream_t q : {r.comm, r.gemm[0], r.gemm[1]}) {
-        if (hipStreamSynchronize(q) != hipSuccess || hipStreamDestroy(q) != hipSuccess)
-          return MOE_ERR_HIP;
-      }
-      r.init = false;
-    }
-    const int cus = device_cus();
-    r.comm = r.gemm[0] = r.gemm[1] = nullptr;
-    bool ok = true;
-    if (comm_cus > 0) {
-      if (comm_cus >= cus) return MOE_ERR_INVALID_ARG;
-      // CU mask bits: the first comm_cus bits of the mask go to the
-      // communication stream, the rest to the GEMM streams
-      std::vector<uint32_t> cm((cus + 31) / 32, 0u), gm((cus + 31) / 32, 0u);
-      for (int i = 0; i < cus; i++) (i < comm_cus ? cm : gm)[i / 32] |= 1u << (i % 32);
-      ok = hipExtStreamCreateWithCUMask(&r.comm, (uint32_t)cm.size(), cm.data()) == hipSuccess &&
-           hipExtStreamCreateWithCUMask(&r.gemm[0], (uint32_t)gm.size(), gm.data()) ==
-               hipSuccess &&
-           hipExtStreamCreateWithCUMask(&r.gemm[1], (uint32_t)gm.size(), gm.data()) == hipSuccess;
-    } else {
-      for (hipStream_t *q : {&r.comm, &r.gemm[0], &r.gemm[1]})
-        ok = ok && hipStreamCreateWithFlags(q, hipStreamNonBlocking) == hipSuccess;
-    }
-    if (!ok) {  // drop whatever was created; the next call tries again
-      for (hipStream_t q : {r.comm, r.gemm[0], r.gemm[1]})
-        if (q) hipStreamDestroy(q);
-      r.comm = r.gemm[0] = r.gemm[1] = nullptr;
-      return MOE_ERR_HIP;
-    }
-    r.comm_cus = comm_cus;
-    r.init = true;
+  PipeDev &pd = g_pipe[dev];
+  PipeStreams *set = nullptr;
+  for (int i = 0; i < pd.n_sets; i++)
+    if (pd.sets[i].comm_cus == comm_cus) set = &pd.sets[i];
+  if (!set) {
+    if (pd.n_sets == kMaxStreamSets) return MOE_ERR_UNSUPPORTED;
+    int rc = create_stream_set(comm_cus, &pd.sets[pd.n_sets]);
+    if (rc) return rc;
+    set = &pd.sets[pd.n_sets++];
   }
-  while (r.ev.size() < n_events) {
+  while (pd.ev.size() < n_events) {
     hipEvent_t e;
     if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return MOE_ERR_HIP;
-    r.ev.push_back(e);
+    pd.ev.push_back(e);
   }
-  *out = &r;
+  out->comm = set->comm;
+  out->gemm[0] = set->gemm[0];
+  out->gemm[1] = set->gemm[1];
+  out->ev = &pd.ev;
   return MOE_OK;
+}
+
+// Creates (or finds) the stream set of comm_cus on the current device, so
+// that a layer call can refuse a comm_cus it cannot serve before it enqueues
+// anything.
+int pipe_prepare(int comm_cus) {
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  PipeRes res;
+  return pipe_resources(comm_cus, 0, &res);
 }
 
 // Rows per minibatch: the caller's, else enough rows for two full waves of
@@ -683,8 +720,10 @@ long pipe_minibatch(const Dims &d, const moe_sched *sc, bool fwd) {
 struct PipeCtx {
   PipeRes *r;
   hipStream_t s;
-  bool wait(hipStream_t q, int e) const { return hipStreamWaitEvent(q, r->ev[e], 0) == hipSuccess; }
-  bool rec(hipStream_t q, int e) const { return hipEventRecord(r->ev[e], q) == hipSuccess; }
+  bool wait(hipStream_t q, int e) const {
+    return hipStreamWaitEvent(q, (*r->ev)[e], 0) == hipSuccess;
+  }
+  bool rec(hipStream_t q, int e) const { return hipEventRecord((*r->ev)[e], q) == hipSuccess; }
   // caller's stream -> all three streams
   bool fork(int e) const {
     return rec(s, e) && wait(r->comm, e) && wait(r->gemm[0], e) && wait(r->gemm[1], e);
@@ -713,9 +752,10 @@ int pipe_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Sa
   const int S = sc->ring_slots > 0 ? sc->ring_slots : 2;
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k, R = (int)d.R;
   std::lock_guard<std::mutex> lock(g_pipe_mu);
-  PipeRes *r = nullptr;
-  int rc = pipe_resources(sc->comm_cus, 3 * (size_t)NM + 5, &r);
+  PipeRes res;
+  int rc = pipe_resources(sc->comm_cus, 3 * (size_t)NM + 5, &res);
   if (rc) return rc;
+  PipeRes *r = &res;
   const int evD = 0, evG1 = NM, evG2 = 2 * NM, evX = 3 * NM, evPlan = 3 * NM + 4;
   const PipeCtx c{r, s};
   if (!c.fork(evX)) return MOE_ERR_HIP;
@@ -795,9 +835,10 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   if (NM > w.max_nm) return MOE_ERR_INVALID_ARG;
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k, R = (int)d.R;
   std::lock_guard<std::mutex> lock(g_pipe_mu);
-  PipeRes *r = nullptr;
-  int rc = pipe_resources(sc->comm_cus, 2 * (size_t)NM + 5, &r);
+  PipeRes res;
+  int rc = pipe_resources(sc->comm_cus, 2 * (size_t)NM + 5, &res);
   if (rc) return rc;
+  PipeRes *r = &res;
   const int evRC = 0, evDG = NM, evX = 2 * NM;
   const PipeCtx c{r, s};
   const bool router = w_router != nullptr;
@@ -1055,6 +1096,10 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   if (mode == MOE_SCHED_PIPELINED && sched->comm_cus < 0) return MOE_ERR_INVALID_ARG;
   Work w;
   if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  if (mode == MOE_SCHED_PIPELINED) {
+    rc = pipe_prepare(sched->comm_cus);  // before anything is enqueued
+    if (rc) return rc;
+  }
   Saved sv;
   carve_saved(d, saved, &sv);
   Packed p;
@@ -1146,6 +1191,10 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   if (mode == MOE_SCHED_PIPELINED && sched->comm_cus < 0) return MOE_ERR_INVALID_ARG;
   Work w;
   if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
+  if (mode == MOE_SCHED_PIPELINED) {
+    rc = pipe_prepare(sched->comm_cus);  // before anything is enqueued
+    if (rc) return rc;
+  }
   Saved sv;
   carve_saved(d, (void *)saved, &sv);
   Packed p;
@@ -1262,6 +1311,9 @@ int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view
   view->dy = w.dy;
   view->dh = w.dh;
   view->dx_rows = w.dX;
+  view->dec_logits = w.dec_logits;
+  view->dec_topk_idx = w.dec_idx;
+  view->dec_topk_w = w.dec_w;
   return MOE_OK;
 }
 

@@ -86,8 +86,9 @@ class MoeLayer:
         return self.saved[off:off + nbytes].view(dtype).view(*shape)
 
     def work_tensor(self, name: str, dtype, shape) -> torch.Tensor:
-        """A view of a backward intermediate left in the workspace (dy, dh,
-        dx_rows), valid until the next call that uses this layer's workspace."""
+        """A view of an intermediate left in the workspace (the backward's dy,
+        dh, dx_rows; the decode forward's dec_logits, dec_topk_idx,
+        dec_topk_w), valid until the next call that uses this workspace."""
         ptr = _lib.moe_workspace_pointers(self.shape, self.ws)[name]
         if not ptr:
             raise KeyError(name)

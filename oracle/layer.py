@@ -287,9 +287,10 @@ def combine(Y, w, inv, k, y_shared=None, exact=False):
     """Combine and final weighted fusion.
 
     Each result goes back to its token's original position [KC §01] and the
-    token's output is the weighted sum of its k expert rows [KC §03 "fusão
-    ponderada final"], in ascending slot order, plus the shared expert's row
-    with weight one; summed in fp64 and stored as bf16.
+    token's output is the weighted sum of its k expert rows (the weighted
+    fusion that closes the measured layer [KC §03]), in ascending slot order,
+    plus the shared expert's row with weight one; summed in fp64 and stored
+    as bf16.
     """
     R = _Round(exact)
     w = np.asarray(w, dtype=np.float64)

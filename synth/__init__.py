@@ -18,7 +18,9 @@ round-to-nearest-even):
 * shared expert weights (when present) likewise, fan-in H / I_s
 * supplied routing: each (token, slot) expert drawn i.i.d. from a categorical
   distribution (Zipf: P(e) proportional to (e+1)^-s, expert 0 hottest), and
-  the k slot weights drawn from a flat Dirichlet (positive, summing to one)
+  the k slot weights of a token the softmax of k i.i.d. N(0, 1) draws
+  (positive, summing to one: what a softmax router gives scores of unit
+  spread), stored as fp32
 * router bias (skewed configurations): +beta on a seeded set of "hot" experts
 * dOut ~ N(0, 1)                                   [T, H]   bf16
 
@@ -134,6 +136,13 @@ def _expert_stack(seq: np.random.SeedSequence, E: int, shape, std: float,
     return out
 
 
+def _softmax_draws(rng: np.random.Generator, T: int, k: int) -> np.ndarray:
+    """[T, k] fp32 slot weights: per token, the softmax of k N(0, 1) draws."""
+    z = rng.standard_normal((T, k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 def _zipf_probs(E: int, s: float) -> np.ndarray:
     p = (np.arange(1, E + 1, dtype=np.float64)) ** (-s)
     return p / p.sum()
@@ -191,7 +200,7 @@ def make_inputs(w: Workload, threads: int = 8, only=None) -> dict:
         else:
             p = _zipf_probs(E, w.zipf_s)
         out["topk_idx"] = rng.choice(E, size=(T, k), p=p).astype(np.int32)
-        out["topk_w"] = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+        out["topk_w"] = _softmax_draws(rng, T, k)
     else:
         raise ValueError(f"unknown routing {w.routing!r}")
     if want("dout"):
@@ -218,5 +227,4 @@ def supplied_routing(T: int, E: int, k: int, seed: int = 0, probs=None):
     rng = np.random.default_rng(np.random.SeedSequence([seed, T, E, k, 7]))
     p = None if probs is None else np.asarray(probs, np.float64) / np.sum(probs)
     idx = rng.choice(E, size=(T, k), p=p).astype(np.int32)
-    wts = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
-    return idx, wts
+    return idx, _softmax_draws(rng, T, k)

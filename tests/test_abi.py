@@ -69,7 +69,10 @@ def test_struct_layouts_match_header():
                        ("moe_work_view", _lib.MoeWorkView)):
         body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (cname, cname), text, re.S).group(1)
         body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
-        fields = re.findall(r"(\w+)\s*;", body)
+        fields = []
+        for decl in body.split(";")[:-1]:
+            fp = re.search(r"\(\s*\*\s*(\w+)\s*\)", decl)       # function pointer
+            fields.append(fp.group(1) if fp else re.findall(r"\w+", decl)[-1])
         assert fields == [f for f, _ in pyt._fields_], cname
 
 

@@ -74,3 +74,43 @@ def test_layer_calls_do_not_wait(mode, mx):
     assert np.array_equal(host(out1), ref[0])
     for k, v in ref[1].items():
         assert np.array_equal(host(g1[k]), v), k
+
+
+def test_alternating_comm_cus_does_not_wait():
+    """Layer calls whose CU split alternates between calls: each split has its
+    own set of streams, kept between calls, so no call waits for the device."""
+    w = synth.custom(T=512, H=512, E=16, k=4, I=256, routing="supplied", zipf_s=1.0, seed=5)
+    note("async: alternating comm_cus 0 / 16 / 0 / 16")
+    inp = synth.make_inputs(w)
+    d = {k: dev(v) for k, v in inp.items() if v is not None and k != "hot"}
+    layer = m.MoeLayer(shape_of(w))
+    layer.prepare(d["w_gate"], d["w_up"], d["w_down"])
+
+    def sc(cus):
+        s = _sched(m.MOE_SCHED_PIPELINED)
+        s.comm_cus = cus
+        return s
+
+    def run(cus):
+        out = layer.forward(d["x"], topk_idx=d["topk_idx"], topk_w=d["topk_w"], sched=sc(cus))
+        g = layer.backward(d["dout"], d["x"], sched=sc(cus))
+        return out, g
+
+    out0, g0 = run(0)
+    torch.cuda.synchronize()
+    ref = (host(out0).copy(), {k: host(v).copy() for k, v in g0.items()})
+    run(16)                                  # first use of this split creates its streams
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    torch.cuda._sleep(200_000_000)
+    t0 = time.perf_counter()
+    results = [run(cus) for cus in (0, 16, 0, 16)]
+    t_call = time.perf_counter() - t0
+    busy = not stream.query()
+    torch.cuda.synchronize()
+    note(f"  four calls returned after {t_call * 1e3:.2f} ms; stream busy: {busy}")
+    assert busy, "a layer call waited for the device"
+    for out, g in results:
+        assert np.array_equal(host(out), ref[0])
+        for k, v in ref[1].items():
+            assert np.array_equal(host(g[k]), v), k

@@ -3,7 +3,10 @@
 The decode path computes the layer's output with its own weight-streaming
 kernels (fp32 dot products summed in a different order than the MFMA
 tiles), so it is compared with the oracle at the bf16 tolerance, and with
-moe_layer_fwd on the same inputs at the same tolerance.  Cases: one token,
+moe_layer_fwd on the same inputs at the same tolerance.  With a router, the
+oracle routes from the decode path's own fp32 logits (read from the
+workspace), and the decode's selection must equal the oracle's for every
+token, weights within 1e-5.  Cases: one token,
 a few tokens, a token count that is not a multiple of anything, experts with
 more than one 64-row pass (supplied routing with duplicates), unused experts,
 the shared expert, the Kimi-shaped dimensions, top-k above 8 (router and
@@ -16,7 +19,7 @@ import torch
 import mixture_experts_layer_offsets_amd as m
 import oracle
 import synth
-from gpu_util import TOL_BF16, bf, check_rel, dev, host, note, shape_of
+from gpu_util import TOL_BF16, bf, check_rel, dev, host, note, oracle_forward, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -63,21 +66,25 @@ def test_decode_matches_oracle(name):
                   d.get("ws_down"))
     out = layer.decode(d["x"], w_router=d.get("w_router"), bias=d.get("bias"),
                        topk_idx=d.get("topk_idx"), topk_w=d.get("topk_w"))
+    torch.cuda.synchronize()
+    if w.routing == "router":
+        # the decode path's own routing, left in the workspace: the oracle's
+        # top-k runs on its fp32 logits, and the selection must match exactly
+        T, k, E = w.T, w.k, w.E
+        L = host(layer.work_tensor("dec_logits", torch.float32, (T, E)))
+        fw = oracle_forward(inp, w, L)
+        assert np.array_equal(host(layer.work_tensor("dec_topk_idx", torch.int32, (T, k))),
+                              fw["idx"])
+        wts = host(layer.work_tensor("dec_topk_w", torch.float32, (T, k)))
+        assert np.abs(wts - fw["w"]).max() <= 1e-5
+    else:
+        fw = oracle.forward(inp, w.k)
+    out_h = bf(out).copy()
     ref = layer.forward(d["x"], w_router=d.get("w_router"), bias=d.get("bias"),
                         topk_idx=d.get("topk_idx"), topk_w=d.get("topk_w"))
     torch.cuda.synchronize()
-    fw = oracle.forward(inp, w.k)
-    if w.routing == "router":
-        # both GPU paths route from the same fp32 logits kernel; the oracle's
-        # fp64 logits may order a near-tie differently, so compare the
-        # routing first and only where it agrees
-        idx = host(layer.saved_tensor("topk_idx", torch.int32, (w.T, w.k)))
-        ok = np.all(idx == fw["idx"], axis=1)
-        assert ok.mean() > 0.9, ok.sum()
-    else:
-        ok = np.ones(w.T, bool)
-    check_rel("out vs oracle", bf(out)[ok], fw["out"][ok], TOL_BF16)
-    check_rel("out vs layer forward", bf(out), bf(ref), TOL_BF16)
+    check_rel("out vs oracle", out_h, fw["out"], TOL_BF16)
+    check_rel("out vs layer forward", out_h, bf(ref), TOL_BF16)
 
 
 def test_decode_deterministic():

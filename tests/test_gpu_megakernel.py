@@ -17,7 +17,8 @@ import torch
 import mixture_experts_layer_offsets_amd as m
 import oracle
 import synth
-from gpu_util import TOL_BF16, TOL_MX, bf, check_rel, dev, host, note, shape_of
+from gpu_util import (TOL_BF16, bf, check_rel, check_routing_layout, dev, host, note,
+                      oracle_forward, shape_of)
 
 # The persistent forward is switched off in libmoe (moe_layer_fwd refuses
 # use_megakernel with MOE_ERR_UNSUPPORTED): its first two GPU runs never
@@ -149,11 +150,10 @@ def test_megakernel_against_oracle():
     note("megakernel vs oracle: shared-router")
     pair = Pair(w)
     out = pair.forward(1, mk_sched(minibatch_rows=512, ring_slots=2, comm_cus=4))
-    fw = oracle.forward(pair.inp, w.k)
-    idx = host(pair.layers[1].saved_tensor("topk_idx", torch.int32, (w.T, w.k)))
-    ok = np.all(idx == fw["idx"], axis=1)
-    assert ok.mean() > 0.99
-    check_rel("out", bf(out)[ok], fw["out"][ok], TOL_BF16)
+    L = host(pair.layers[1].saved_tensor("logits", torch.float32, (w.T, w.E)))
+    fw = oracle_forward(pair.inp, w, L)
+    check_routing_layout(pair.layers[1], w, fw)
+    check_rel("out", bf(out), fw["out"], TOL_BF16)
 
 
 def test_megakernel_watchdog_reports_timeout():

@@ -17,9 +17,8 @@ import torch
 import mixture_experts_layer_offsets_amd as m
 import oracle
 import synth
-from gpu_util import TOL_MX, Run, bf, check_rel, dev, host, note, unblock_scales
-from oracle.mx import e4m3_decode, e4m3_encode, mx_dequantize
-from oracle.numerics import bf16_bits
+from gpu_util import (TOL_MX, Run, bf, check_layer_mx, check_rel, dev, host, logits_of, note,
+                      oracle_forward, unblock_scales)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,131 +121,12 @@ MX_CASES = {
 }
 
 
-def _quantise_at(v, s):
-    """Values of the E4M3 codes of v at the block scale 2^s (s broadcast per
-    element): the oracle's element conversion with the scale given."""
-    sc = np.clip(np.ldexp(v, -s), -448.0, 448.0)
-    return e4m3_decode(e4m3_encode(sc)) * np.ldexp(1.0, s)
-
-
-def _block_scale(amax):
-    _, ex = np.frexp(amax)
-    return np.where(amax > 0, np.clip(ex.astype(np.int64) - 1 - 8, -127, 127), -127)
-
-
-def _check_act_codes(aq, as_, fw, K):
-    """The SwiGLU epilogue's MX codes of a against the oracle.
-
-    The GPU forms g and u by fp32 accumulation in its own order; any order
-    keeps |g_gpu - g| <= gamma * sum_h |x_h w_h| with gamma = K 2^-24 / (1 -
-    K 2^-24) (the standard bound of recursive summation), likewise u.  From
-    these bounds (and a few ulps for silu and the product) each element's a
-    lies in [a - da, a + da]; the GPU's block scale must be the scale of some
-    block maximum in the resulting range, and each GPU code must be the code,
-    at that scale, of some value in its element's range (quantisation is
-    monotone).  Codes equal to the oracle's need no bound; the fraction of the
-    others is reported.
-    """
-    W, Xh, off = fw["W"], fw["Xhat"], fw["offsets"]
-    g, u = fw["g"], fw["u"]
-    Sg = np.zeros_like(g)
-    Su = np.zeros_like(u)
-    for e in range(len(off) - 1):
-        rs = slice(int(off[e]), int(off[e + 1]))
-        if rs.stop > rs.start:
-            Sg[rs] = np.abs(Xh[rs]) @ np.abs(W["g"][e])
-            Su[rs] = np.abs(Xh[rs]) @ np.abs(W["u"][e])
-    eps = 2.0 ** -24
-    gamma = K * eps / (1 - K * eps) + eps          # + the final fp32 rounding of g, u
-    dg, du = gamma * Sg, gamma * Su
-    sg = 1.0 / (1.0 + np.exp(-g))
-    a = g * sg * u
-    # |silu'| <= 1.1 everywhere; 16 ulps for silu (hardware exp) and the product
-    da = 1.1 * (np.abs(u) + du) * dg + np.abs(g * sg) * du + 16 * eps * np.abs(a) + 1e-38
-    got = mx_dequantize(aq, as_, axis=1)
-    s_gpu = np.repeat(as_.astype(np.int64) - 127, 32, axis=1)
-    R, I = a.shape
-    amax_lo = np.maximum(np.abs(a) - da, 0).reshape(R, -1, 32).max(axis=2)
-    amax_hi = (np.abs(a) + da).reshape(R, -1, 32).max(axis=2)
-    s_lo = np.repeat(_block_scale(amax_lo), 32, axis=1)
-    s_hi = np.repeat(_block_scale(amax_hi), 32, axis=1)
-    assert np.all((s_gpu >= s_lo) & (s_gpu <= s_hi)), "act: block scale outside its range"
-    lo = _quantise_at(a - da, s_gpu)
-    hi = _quantise_at(a + da, s_gpu)
-    diff = got != fw["ahat"]
-    bad = diff & ((got < lo) | (got > hi))
-    assert not bad.any(), f"act: {bad.sum()} codes outside the range the fp32 bound allows"
-    return float(diff.mean())
-
-
-def check_layer_mx(run, fw, bw, tol=TOL_MX):
-    w = run.w
-    T, k, E, H, I = w.T, w.k, w.E, w.H, w.I
-    R = T * k
-    idx = host(run.saved("topk_idx", torch.int32, (T, k)))
-    amb = np.zeros(T, bool)
-    if fw["logits"] is not None:
-        L = host(run.saved("logits", torch.float32, (T, E)))
-        check_rel("logits", L, fw["logits"], 1e-4)
-        ref_idx = fw["idx"]
-        amb = np.any(idx != ref_idx, axis=1)
-        d = np.abs(L - fw["logits"]).max()
-        for t in np.flatnonzero(amb):
-            sel = fw["logits"][t, idx[t]]
-            assert sel.min() >= np.sort(fw["logits"][t])[-k] - 2 * d
-        assert amb.mean() < 0.01
-    ok = ~amb
-    assert np.array_equal(idx[ok], fw["idx"][ok])
-    wts = host(run.saved("topk_w", torch.float32, (T, k)))
-    assert np.abs(wts[ok] - fw["w"][ok]).max() <= 1e-5
-    perm = host(run.saved("perm", torch.int32, (R,)))
-    # dispatch: codes, scales and round trip of the rows the GPU laid out
-    codes, scales = oracle.dispatch(run.inp["x"], perm, k, mx=True)
-    assert np.array_equal(host(run.saved("x_perm", torch.uint8, (R, H))), codes)
-    xs = unblock_scales(host(run.saved("x_scale", torch.uint8, (R, H // 32))), R, H)
-    assert np.array_equal(xs, scales)
-    xh = host(run.saved("x_hat", torch.int16, (R, H))).view(np.uint16)
-    assert np.array_equal(xh, bf16_bits(mx_dequantize(codes, scales, axis=1)))
-    # the activation's codes and its bf16 round trip agree with each other
-    aq = host(run.saved("act_q", torch.uint8, (R, I)))
-    as_ = unblock_scales(host(run.saved("act_scale", torch.uint8, (R, I // 32))), R, I)
-    act = bf(run.saved("act", torch.int16, (R, I)))
-    assert np.array_equal(act, mx_dequantize(aq, as_, axis=1))
-    if not amb.any():
-        assert np.array_equal(host(run.saved("counts", torch.int32, (E,))), fw["counts"])
-        assert np.array_equal(host(run.saved("offsets", torch.int32, (E + 1,))), fw["offsets"])
-        assert np.array_equal(perm, fw["perm"])
-        assert np.array_equal(host(run.saved("inv_perm", torch.int32, (R,))), fw["inv"])
-        frac = _check_act_codes(aq, as_, fw, H)
-        note(f"  act: {frac:.2e} of the codes differ from the oracle's, all within the "
-             f"fp32 accumulation bound")
-        check_rel("y", bf(run.saved("y", torch.int16, (R, H))), fw["Y"], tol)
-    check_rel("out", bf(run.out)[ok], fw["out"][ok], tol)
-    if bw is None:
-        return
-    g = run.grads
-    check_rel("dx", bf(g["dx"])[ok], bw["dx"][ok], tol)
-    if not amb.any():
-        check_rel("dW_gate", host(g["dw_gate"]), bw["dWg"], tol)
-        check_rel("dW_up", host(g["dw_up"]), bw["dWu"], tol)
-        check_rel("dW_down", host(g["dw_down"]), bw["dWd"], tol)
-        check_rel("dtopk_w", host(g["dtopk_w"]), bw["dw"], tol)
-        if fw["logits"] is not None:
-            check_rel("dW_router", host(g["dw_router"]), bw["dWr"], tol)
-        if w.shared_I:
-            Is = w.shared_I
-            dws = host(g["dws"])
-            check_rel("dWs_gate", dws[:H * Is].reshape(H, Is), bw["dWsg"], tol)
-            check_rel("dWs_up", dws[H * Is:2 * H * Is].reshape(H, Is), bw["dWsu"], tol)
-            check_rel("dWs_down", dws[2 * H * Is:].reshape(Is, H), bw["dWsd"], tol)
-
-
 @pytest.mark.parametrize("name", list(MX_CASES))
 def test_layer_mx_small(name):
     w = MX_CASES[name]
     note(f"layer {name}: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} shared={w.shared_I}")
     run = Run(w)
-    fw = oracle.forward(run.inp, w.k, mx=True)
+    fw = oracle_forward(run.inp, w, logits_of(run))
     bw = oracle.backward(run.inp, fw)
     check_layer_mx(run, fw, bw)
     if name == "mx-one-expert":
@@ -262,7 +142,7 @@ def test_layer_mx_mid():
                      router_std=1 / 32, mx=True, seed=4)
     note(f"layer mid-mx: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
     run = Run(w)
-    fw = oracle.forward(run.inp, w.k, mx=True)
+    fw = oracle_forward(run.inp, w, logits_of(run))
     bw = oracle.backward(run.inp, fw)
     check_layer_mx(run, fw, bw)
     # the same inputs twice give the same bits
