@@ -308,7 +308,10 @@ def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R, mx_wgrad=False):
     """Backward of one expert's SwiGLU FFN given its rows' output gradient dY.
 
     ``Wb`` holds the expert's weights as the backward data-gradient GEMMs see
-    them (:meth:`ExpertWeights.bwd`).
+    them (:meth:`ExpertWeights.bwd`).  ``g`` and ``u`` are the forward's fp32
+    accumulator values; they reach the backward as the layer stores its
+    activations, as bf16 (the layer's precision is bf16 activations with fp32
+    accumulation), and the SwiGLU backward uses those stored values.
 
     dA = dY' Wd^T; dg = dA u silu'(g); du = dA silu(g) (stored as bf16);
     dWd = ahat^T dY; dWg = Xhat^T dg; dWu = Xhat^T du (fp32);
@@ -320,6 +323,7 @@ def _swiglu_rows_bwd(Xhat, g, u, ahat, dY, Wb, mx, R, mx_wgrad=False):
     at the expert's first row (the last block zero-padded).
     silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
     """
+    g, u = R.bf16(g), R.bf16(u)              # stored activations
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
     dA = R.f32(dYq @ Wb["d"].T)
     s = sigmoid(g)
@@ -578,6 +582,7 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, wei
     ah = mx_roundtrip(a, axis=1) if mx else R.bf16(a)
     dYq = mx_roundtrip(dY, axis=1) if mx else dY
     dA = R.f32(dYq @ Wb["d"][bc, :].T)
+    g, u = R.bf16(g), R.bf16(u)              # stored activations (see _swiglu_rows_bwd)
     s = sigmoid(g)
     dg = R.bf16(dA * u * s * (1.0 + g * (1.0 - s)))
     du = R.bf16(dA * g * s)

@@ -80,6 +80,40 @@ def test_one_expert_top1_is_dense_swiglu():
     assert np.array_equal(fw["out"], y.numpy())
 
 
+def test_one_expert_top1_backward_is_dense_swiglu_backward():
+    """The backward of one expert with top-1 routing against a dense SwiGLU
+    backward written with torch: silu's derivative from torch's autograd, the
+    bf16 and fp32 rounding points by torch's casts (saved g, u as bf16
+    activations; dg, du, dX, dx stored as bf16; weight gradients in fp32)."""
+    w = small(E=1, k=1, routing="supplied")
+    inp = synth.make_inputs(w)
+    fw = oracle.forward(inp, 1)
+    bw = oracle.backward(inp, fw)
+
+    def t(name, e=None):
+        a = inp[name] if e is None else inp[name][e]
+        return torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+    x, dout = t("x"), t("dout")
+    Wg, Wu, Wd = t("w_gate", 0), t("w_up", 0), t("w_down", 0)
+    f32 = lambda v: v.to(torch.float32).to(torch.float64)           # noqa: E731
+    g = _bf16_torch(f32(x @ Wg)).requires_grad_()
+    u = _bf16_torch(f32(x @ Wu)).requires_grad_()
+    a = _bf16_torch(f32(torch.nn.functional.silu(f32(x @ Wg)) * f32(x @ Wu)))
+    dA = f32(dout @ Wd.T)
+    (torch.nn.functional.silu(g) * u).backward(dA)
+    dg, du = _bf16_torch(g.grad), _bf16_torch(u.grad)
+    dX = _bf16_torch(dg @ Wg.T + du @ Wu.T)
+    assert np.array_equal(bw["dx"], dX.numpy())
+    assert np.array_equal(bw["dWd"][0], f32(a.T @ dout).numpy())
+    assert np.array_equal(bw["dWg"][0], f32(x.T @ dg).numpy())
+    assert np.array_equal(bw["dWu"][0], f32(x.T @ du).numpy())
+    # g, u enter the backward as bf16: with fp32 g, u the gradients differ
+    g32 = f32(x @ Wg).requires_grad_()
+    u32 = f32(x @ Wu).requires_grad_()
+    (torch.nn.functional.silu(g32) * u32).backward(dA)
+    assert not np.array_equal(_bf16_torch(g32.grad).numpy(), dg.numpy())
+
+
 @pytest.mark.parametrize("k", [1, 3])
 def test_permute_unpermute_identity(k):
     T, E, H = 40, 5, 16
