@@ -304,7 +304,8 @@ class Bench:
                 def fn(_user, stage):
                     if stage in stages:
                         flush.fill_(stage)
-                return self.m.STAGE_HOOK(fn)
+                return _lib.STAGE_HOOK(fn)
+            from mixture_experts_layer_offsets_amd import _lib
             hooks = (mk(FLUSH_FWD), mk(FLUSH_BWD))
             self._keep.extend(hooks)
         for _ in range(self.a.warmup):
