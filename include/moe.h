@@ -212,6 +212,23 @@ int moe_layout(const moe_shape *shape, const int32_t *topk_idx,
                int32_t *counts, int32_t *offsets, int32_t *perm,
                int32_t *inv_perm, void *ws, size_t ws_bytes, void *stream);
 
+/* Layout without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same results as moe_layout, bit for bit, with its
+ * scratch (per-chunk expert counts, tile prefix, expert order) in a static
+ * device array of the library, 4 MiB per device, held until the process
+ * ends.  Shapes whose scratch exceeds it -- ceil(T*k / 1024) * E + 2E + 1
+ * int32 words, each of the three pieces rounded up to 256 bytes -- return
+ * MOE_ERR_WORKSPACE and enqueue nothing.  The call allocates nothing and
+ * does not wait for the device.  Every call on one device shares that
+ * device's array: calls whose work overlaps on the device (different
+ * streams, or several threads) race and give undefined results; calls
+ * ordered on one stream are safe.  Arguments and errors otherwise as
+ * moe_layout. */
+int moe_layout_noalloc(const moe_shape *shape, const int32_t *topk_idx,
+                       int32_t *counts, int32_t *offsets, int32_t *perm,
+                       int32_t *inv_perm, void *stream);
+
 /* Dispatch (gather-permute): row r of x_perm is a copy of token
  * perm[r] / k of x -- the destination-driven read the pages call pull
  * dispatch [KC §02].  bf16: x_perm is uint16_t [R][H], x_scale unused.

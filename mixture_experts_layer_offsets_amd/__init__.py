@@ -9,7 +9,8 @@ from ._lib import (MOE_BF16, MOE_ERR_DEVICE_TIMEOUT, MOE_MXFP8, MOE_OK, MoeError
                    MOE_SCHED_PERSISTENT, MOE_SCHED_PIPELINED, MOE_SCHED_STAGED,
                    MoeSched, Shape, load,
                    moe_combine, moe_decode_fwd, moe_dispatch, moe_expert_ffn, moe_layer_bwd, moe_layer_fwd,
-                   moe_layout, moe_packed_weight_bytes, moe_prepare_weights, moe_read_status,
+                   moe_layout, moe_layout_noalloc, moe_packed_weight_bytes, moe_prepare_weights,
+                   moe_read_status,
                    moe_route, moe_router_logits, moe_saved_bytes, moe_saved_pointers,
                    moe_strerror, moe_workspace_bytes, moe_workspace_pointers)
 from .layer import MoeLayer  # noqa: F401

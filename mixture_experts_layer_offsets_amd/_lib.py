@@ -64,6 +64,7 @@ SIGNATURES = {
     "moe_router_logits": (c_int, [c_void_p] + [c_void_p] * 4 + [c_void_p, c_size_t, c_void_p]),
     "moe_route": (c_int, [c_void_p] * 4 + [c_void_p]),
     "moe_layout": (c_int, [c_void_p] * 6 + [c_void_p, c_size_t, c_void_p]),
+    "moe_layout_noalloc": (c_int, [c_void_p] * 6 + [c_void_p]),
     "moe_dispatch": (c_int, [c_void_p] * 5 + [c_void_p]),
     "moe_expert_ffn": (c_int, [c_void_p] * 6 + [c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [c_void_p] * 6 + [c_void_p]),
@@ -177,6 +178,11 @@ def moe_layout(shape, topk_idx, counts, offsets, perm, inv_perm, ws, stream=None
     _ck(load().moe_layout(_shape(shape), _p(topk_idx), _p(counts), _p(offsets), _p(perm),
                           _p(inv_perm), _p(ws), ws.numel() * ws.element_size(),
                           _stream(stream)), "moe_layout")
+
+
+def moe_layout_noalloc(shape, topk_idx, counts, offsets, perm, inv_perm, stream=None):
+    _ck(load().moe_layout_noalloc(_shape(shape), _p(topk_idx), _p(counts), _p(offsets),
+                                  _p(perm), _p(inv_perm), _stream(stream)), "moe_layout_noalloc")
 
 
 def moe_dispatch(shape, x, perm, x_perm, x_scale=None, stream=None):

@@ -909,6 +909,49 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   return hip_status();
 }
 
+// ---- allocation-free layout (moe_layout_noalloc)
+//
+// Its scratch (the per-chunk expert counts, the tile prefix and the expert
+// order) lives in this file-scope device array instead of a caller's
+// workspace.  Host code never passes the array's name to a kernel: that name
+// is a host-side stand-in, not a device address.  Each device's own copy is
+// found once, on the first call on that device, with hipGetSymbolAddress.
+
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {nullptr};
+
+int noalloc_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The pieces of the layout's scratch, carved like the workspace.
+struct LayoutScratch {
+  int32_t *chunk_counts, *tile_start, *order;
+};
+
+size_t carve_layout_scratch(const Dims &d, void *base, LayoutScratch *ls) {
+  Carver c(base);
+  LayoutScratch t{};
+  const long nchunks = (d.R + kLayoutChunk - 1) / kLayoutChunk;
+  t.chunk_counts = c.take<int32_t>(nchunks * d.E);
+  t.tile_start = c.take<int32_t>(d.E + 1);
+  t.order = c.take<int32_t>(d.E);
+  if (ls) *ls = t;
+  return c.off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1003,6 +1046,26 @@ int moe_layout(const moe_shape *shape, const int32_t *topk_idx, int32_t *counts,
   if (ws_bytes < carve_work(d, ws, &w)) return MOE_ERR_WORKSPACE;
   launch_layout(topk_idx, (int)d.R, (int)d.E, w.chunk_counts, counts, offsets, perm, inv_perm,
                 w.tile_start, kTileM, w.order, S(stream));
+  return hip_status();
+}
+
+int moe_layout_noalloc(const moe_shape *shape, const int32_t *topk_idx, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!topk_idx || !counts || !offsets || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
+  if (carve_layout_scratch(d, nullptr, nullptr) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void *base = nullptr;
+  rc = noalloc_scratch(&base);
+  if (rc) return rc;
+  LayoutScratch ls;
+  carve_layout_scratch(d, base, &ls);
+  // every scratch word is written before it is read (the count pass fills
+  // the whole chunk table, the scan pass the tile prefix and the order), so
+  // nothing is cleared
+  launch_layout(topk_idx, (int)d.R, (int)d.E, ls.chunk_counts, counts, offsets, perm, inv_perm,
+                ls.tile_start, kTileM, ls.order, S(stream));
   return hip_status();
 }
 

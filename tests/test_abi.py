@@ -220,3 +220,14 @@ def test_workspace_pointers(lib):
     assert lib.moe_workspace_pointers(ctypes.byref(bad.c()), base,
                                       ctypes.byref(view)) == _lib.MOE_ERR_INVALID_ARG
     assert view.dy is None and view.dh is None
+
+
+def test_layout_noalloc_refuses_oversized_shapes_before_any_device_work(lib):
+    """Its scratch is a 4 MiB static array: a shape needing more is refused
+    with MOE_ERR_WORKSPACE before any HIP call (so this runs without a GPU)."""
+    big = ctypes.byref(m.Shape(1 << 19, 64, 1024, 8, 64).c())     # 16 MiB of chunk counts
+    fake = 1 << 40
+    assert lib.moe_layout_noalloc(big, fake, fake, fake, fake, fake, None) == \
+        _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_layout_noalloc(big, None, fake, fake, fake, fake, None) == \
+        _lib.MOE_ERR_INVALID_ARG
