@@ -17,8 +17,9 @@ Kimi-shaped configuration's stated minibatch) is reported beside it.  The
 per-stage times, MFMA fractions and the roofline come from a staged pass with
 HIP events around every kernel on the layer's stream; the permute stages'
 HBM fractions come from a second staged pass in which 1 GiB of scratch is
-written right before each of those stages (so the 256 MB Infinity Cache
-holds none of their inputs).
+written and then read back right before each of those stages (the 256 MB
+Infinity Cache then holds none of their inputs, and no dirty lines that the
+timed stage would have to write back).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule staged|pipelined] [--minibatch-rows N]
@@ -119,9 +120,9 @@ def _algorithmic(w):
         "gemm_dgrad_gate_up": 4.0 * R * H * I,
         "gemm_wgrad_gate_up": 4.0 * R * H * I,
     }
-    # bytes per element of a dispatched row: bf16, or an E4M3 code plus a
-    # 1/32 share of an E8M0 scale
-    xb = 1.0 + 1.0 / 32 if w.mx else 2.0
+    # bytes per element of a dispatched row: bf16, or an E4M3 code, a 1/32
+    # share of an E8M0 scale and the bf16 round trip the weight gradients read
+    xb = 1.0 + 1.0 / 32 + 2.0 if w.mx else 2.0
     b = {
         # unique token rows read once, routed rows written once, + indices
         "dispatch": T * H * 2 + R * H * xb + R * 4,
@@ -296,14 +297,21 @@ class Bench:
     def staged_stages(self, flush=None):
         """Per-stage ms of the staged schedule (HIP events on the layer's
         stream around every stage).  With ``flush`` (a device buffer), the
-        buffer is overwritten right before the stages named in FLUSHED."""
+        buffer is overwritten and read back right before the stages named in
+        FLUSH_FWD / FLUSH_BWD."""
         np, torch = self.np, self.torch
         hooks = (None, None)
         if flush is not None:
             def mk(stages):
                 def fn(_user, stage):
                     if stage in stages:
+                        # write the scratch, then read it back: the write
+                        # evicts the Infinity Cache, the read leaves it
+                        # holding clean, unrelated lines (a write alone
+                        # leaves dirty lines the timed stage would have to
+                        # write back)
                         flush.fill_(stage)
+                        flush.view(torch.int32).sum()
                 return _lib.STAGE_HOOK(fn)
             from mixture_experts_layer_offsets_amd import _lib
             hooks = (mk(FLUSH_FWD), mk(FLUSH_BWD))

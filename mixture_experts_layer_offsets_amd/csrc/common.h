@@ -54,6 +54,14 @@ __device__ __forceinline__ uint4 ld_once(const uint4 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A 16-byte store of data this layer does not read again (non-temporal: it
+// does not allocate lines that would evict data read again).
+__device__ __forceinline__ void st_once(uint4 *p, const uint4 &v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, (u32x4 *)p);
+}
+
 // Wave-wide sum (fixed butterfly order -> deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -109,10 +109,12 @@ void launch_dispatch_mx(const uint16_t *x, const int32_t *perm, uint8_t *xq, uin
 // sorted rows inv[t*k + j].  Same result as the gather above; it reads each
 // token once instead of k times.  Grid (H/8 chunks over 128 threads, T).
 
-// Only rows in [r0, r1) are written (one minibatch of sorted rows; the whole
-// set is [0, T*k)).  KMAX bounds k (8 or kMaxTopKPush): no index loads past
-// the bound.
-template <int KMAX>
+// Only rows in [r0, r1) are written (one minibatch of sorted rows; RANGE =
+// false is the whole set [0, T*k) and carries no test).  KMAX bounds k (8 or
+// kMaxTopKPush): no index loads past the bound.  The token's chunk is loaded
+// before the row indices resolve (it is in bounds either way), so its load
+// overlaps theirs instead of waiting for a test that depends on them.
+template <int KMAX, bool RANGE>
 __global__ __launch_bounds__(128) void dispatch_push_bf16_kernel(const uint4 *__restrict__ x,
                                                                  const int32_t *__restrict__ inv,
                                                                  uint4 *__restrict__ xp, int k,
@@ -120,18 +122,13 @@ __global__ __launch_bounds__(128) void dispatch_push_bf16_kernel(const uint4 *__
   const int t = blockIdx.y;
   const int c = blockIdx.x * 128 + threadIdx.x;
   if (c >= HC) return;
-  int row[KMAX];
-  bool any = false;
-#pragma unroll
-  for (int j = 0; j < KMAX; j++) {
-    row[j] = inv[t * k + min(j, k - 1)];
-    any |= j < k && row[j] >= r0 && row[j] < r1;
-  }
-  if (!any) return;
   const uint4 v = ld_once(x + (size_t)t * HC + c);
+  int row[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) row[j] = inv[t * k + min(j, k - 1)];
 #pragma unroll
   for (int j = 0; j < KMAX; j++)
-    if (j < k && row[j] >= r0 && row[j] < r1) xp[(size_t)row[j] * HC + c] = v;
+    if (j < k && (!RANGE || (row[j] >= r0 && row[j] < r1))) xp[(size_t)row[j] * HC + c] = v;
 }
 
 void launch_dispatch_push_bf16_range(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T,
@@ -139,12 +136,19 @@ void launch_dispatch_push_bf16_range(const uint16_t *x, const int32_t *inv, uint
   const int HC = H / 8;
   if (T <= 0) return;
   const dim3 g((HC + 127) / 128, T), b(128);
-  if (k <= 8)
-    hipLaunchKernelGGL(dispatch_push_bf16_kernel<8>, g, b, 0, s, (const uint4 *)x, inv,
+  const bool all = r0 <= 0 && r1 >= T * k;
+  if (k <= 8 && all)
+    hipLaunchKernelGGL((dispatch_push_bf16_kernel<8, false>), g, b, 0, s, (const uint4 *)x, inv,
                        (uint4 *)xp, k, HC, r0, r1);
+  else if (k <= 8)
+    hipLaunchKernelGGL((dispatch_push_bf16_kernel<8, true>), g, b, 0, s, (const uint4 *)x, inv,
+                       (uint4 *)xp, k, HC, r0, r1);
+  else if (all)
+    hipLaunchKernelGGL((dispatch_push_bf16_kernel<kMaxTopKPush, false>), g, b, 0, s,
+                       (const uint4 *)x, inv, (uint4 *)xp, k, HC, r0, r1);
   else
-    hipLaunchKernelGGL(dispatch_push_bf16_kernel<kMaxTopKPush>, g, b, 0, s, (const uint4 *)x,
-                       inv, (uint4 *)xp, k, HC, r0, r1);
+    hipLaunchKernelGGL((dispatch_push_bf16_kernel<kMaxTopKPush, true>), g, b, 0, s,
+                       (const uint4 *)x, inv, (uint4 *)xp, k, HC, r0, r1);
 }
 
 void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *xp, int T, int k,
@@ -154,9 +158,11 @@ void launch_dispatch_push_bf16(const uint16_t *x, const int32_t *inv, uint16_t *
 
 // MX: each lane quantises 8 values as in dispatch_mx_kernel (a quad of lanes
 // per 32-value block), then stores codes, scale and round trip to k rows.
-// Only rows in [r0, r1) are written.  Whether a token has such a row is the
-// same for the four lanes of a quad (one token), so the quad's block-maximum
-// exchange never mixes a returning lane with a working one.
+// Only rows in [r0, r1) are written (RANGE = false: all rows, no test).
+// Every lane of a quad (one token's 32-value block) runs the conversion, so
+// the quad's block-maximum exchange always has all four lanes; the token's
+// chunk is loaded before the row indices resolve.  KMAX bounds k.
+template <int KMAX, bool RANGE>
 __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
     const uint4 *__restrict__ x, const int32_t *__restrict__ inv, uint2 *__restrict__ xq,
     uint8_t *__restrict__ xs, uint4 *__restrict__ xhat, int T, int k, int HC /* H/8 */, int r0,
@@ -165,23 +171,18 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
   if (id >= (long)T * HC) return;
   const long R = (long)T * k;  // rows of the output (scale plane stride)
   const int t = (int)(id / HC), c = (int)(id - (long)t * HC);
-  int row[kMaxTopKPush];
-  bool any = false;
-#pragma unroll
-  for (int j = 0; j < kMaxTopKPush; j++) {
-    row[j] = inv[t * k + min(j, k - 1)];
-    any |= j < k && row[j] >= r0 && row[j] < r1;
-  }
-  if (!any) return;
   float v[8];
   unpack8(ld_once(x + (size_t)t * HC + c), v);
+  int row[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) row[j] = inv[t * k + min(j, k - 1)];
   uint2 codes;
   float deq[8];
   const uint32_t sc = mx_quad8(v, &codes, deq);
   const uint4 hat = pack8(deq);
 #pragma unroll
-  for (int j = 0; j < kMaxTopKPush; j++) {
-    if (j < k && row[j] >= r0 && row[j] < r1) {
+  for (int j = 0; j < KMAX; j++) {
+    if (j < k && (!RANGE || (row[j] >= r0 && row[j] < r1))) {
       const size_t r = (size_t)row[j];
       xq[r * HC + c] = codes;
       if ((c & 3) == 0) xs[((size_t)(c >> 4) * R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
@@ -195,8 +196,23 @@ void launch_dispatch_push_mx_range(const uint16_t *x, const int32_t *inv, uint8_
                                    int r1, hipStream_t s) {
   const long n = (long)T * (H / 8);
   if (n <= 0) return;
-  hipLaunchKernelGGL(dispatch_push_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const uint4 *)x, inv, (uint2 *)xq, xs, (uint4 *)xhat, T, k, H / 8, r0, r1);
+  const dim3 g((unsigned)((n + 255) / 256)), b(256);
+  const bool all = r0 <= 0 && r1 >= T * k;
+  auto *X = (const uint4 *)x;
+  auto *Q = (uint2 *)xq;
+  auto *Hh = (uint4 *)xhat;
+  if (k <= 8 && all)
+    hipLaunchKernelGGL((dispatch_push_mx_kernel<8, false>), g, b, 0, s, X, inv, Q, xs, Hh, T, k,
+                       H / 8, r0, r1);
+  else if (k <= 8)
+    hipLaunchKernelGGL((dispatch_push_mx_kernel<8, true>), g, b, 0, s, X, inv, Q, xs, Hh, T, k,
+                       H / 8, r0, r1);
+  else if (all)
+    hipLaunchKernelGGL((dispatch_push_mx_kernel<kMaxTopKPush, false>), g, b, 0, s, X, inv, Q, xs,
+                       Hh, T, k, H / 8, r0, r1);
+  else
+    hipLaunchKernelGGL((dispatch_push_mx_kernel<kMaxTopKPush, true>), g, b, 0, s, X, inv, Q, xs,
+                       Hh, T, k, H / 8, r0, r1);
 }
 
 void launch_dispatch_push_mx(const uint16_t *x, const int32_t *inv, uint8_t *xq, uint8_t *xs,
@@ -219,13 +235,18 @@ void launch_quant_rows_mx_range(const uint16_t *src, int row0, int rows, int row
 // Combine + final weighted fusion: out[t] = sum_j w[t,j] y[inv[t*k+j]] (+ ys[t]),
 // fp32 fused multiply-adds in ascending j.  Grid (chunk groups, T).
 
+// One wave per block: measured on MI355X at the Kimi shape (after the cache
+// is flushed), 64-thread blocks gather about 2 % faster than 128 or 256.
+constexpr int kGatherBlock = 64;
+
 template <int KMAX>
-__global__ __launch_bounds__(128) void combine_kernel(const uint16_t *__restrict__ y,
-                                                      const float *__restrict__ w,
-                                                      const int32_t *__restrict__ inv,
-                                                      const uint16_t *__restrict__ ys,
-                                                      uint16_t *__restrict__ out, int k, int HC) {
-  const int c = blockIdx.x * 128 + threadIdx.x;
+__global__ __launch_bounds__(kGatherBlock) void combine_kernel(const uint16_t *__restrict__ y,
+                                                               const float *__restrict__ w,
+                                                               const int32_t *__restrict__ inv,
+                                                               const uint16_t *__restrict__ ys,
+                                                               uint16_t *__restrict__ out, int k,
+                                                               int HC) {
+  const int c = blockIdx.x * kGatherBlock + threadIdx.x;
   if (c < HC) combine8<KMAX>(y, w, inv, ys, out, blockIdx.y, c, k, HC);
 }
 
@@ -233,7 +254,7 @@ void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const
                     uint16_t *out, int T, int k, int H, hipStream_t s) {
   const int HC = H / 8;
   if (T <= 0) return;
-  const dim3 g((HC + 127) / 128, T), b(128);
+  const dim3 g((HC + kGatherBlock - 1) / kGatherBlock, T), b(kGatherBlock);
   if (k <= 8)
     hipLaunchKernelGGL(combine_kernel<8>, g, b, 0, s, y, w, inv, ys, out, k, HC);
   else
@@ -345,12 +366,12 @@ void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float
 // the shared expert's rows exist (the kernel without them carries neither
 // branch nor their registers).
 template <int KMAX, bool ROUTER, bool SHARED>
-__global__ __launch_bounds__(128) void reverse_dispatch_kernel(
+__global__ __launch_bounds__(kGatherBlock) void reverse_dispatch_kernel(
     const uint4 *__restrict__ dX, const int32_t *__restrict__ inv, const int32_t *__restrict__ idx,
     const float *__restrict__ dsel, const uint4 *__restrict__ wrT, const uint4 *__restrict__ dxs,
     uint4 *__restrict__ dx, int k, int HC) {
   const int t = blockIdx.y;
-  const int c = blockIdx.x * 128 + threadIdx.x;
+  const int c = blockIdx.x * kGatherBlock + threadIdx.x;
   if (c >= HC) return;
   // all k row indices, then all k rows' chunks, in flight before the first
   // add (index slots past k repeat the last one)
@@ -388,14 +409,14 @@ __global__ __launch_bounds__(128) void reverse_dispatch_kernel(
 #pragma unroll
     for (int q = 0; q < 8; q++) acc[q] += v[q];
   }
-  dx[(size_t)t * HC + c] = pack8(acc);
+  st_once(dx + (size_t)t * HC + c, pack8(acc));  // not read again by the layer
 }
 
 template <int KMAX>
 static void launch_rd(const dim3 &g, const uint16_t *dX, const int32_t *inv, const int32_t *idx,
                       const float *dsel, const uint16_t *wrT, const uint16_t *dxs, uint16_t *dx,
                       int k, int HC, hipStream_t s) {
-  const dim3 b(128);
+  const dim3 b(kGatherBlock);
   auto *X = (const uint4 *)dX;
   auto *W = (const uint4 *)wrT;
   auto *S = (const uint4 *)dxs;
@@ -419,7 +440,7 @@ void launch_reverse_dispatch(const uint16_t *dX, const int32_t *inv, const int32
                              uint16_t *dx, int T, int k, int H, hipStream_t s) {
   const int HC = H / 8;
   if (T <= 0) return;
-  const dim3 g((HC + 127) / 128, T);
+  const dim3 g((HC + kGatherBlock - 1) / kGatherBlock, T);
   if (k <= 8)
     launch_rd<8>(g, dX, inv, idx, dsel, wrT, dxs, dx, k, HC, s);
   else

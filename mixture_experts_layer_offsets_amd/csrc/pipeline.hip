@@ -250,7 +250,7 @@ __global__ __launch_bounds__(128) void reverse_dispatch_list_kernel(
 #pragma unroll
       for (int q = 0; q < 8; q++) acc[q] += v[q];
     }
-    dx[(size_t)t * HC + c] = pack8(acc);
+    st_once((uint4 *)dx + (size_t)t * HC + c, pack8(acc));  // not read again by the layer
   }
 }
 

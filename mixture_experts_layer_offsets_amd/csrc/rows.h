@@ -52,7 +52,8 @@ __device__ __forceinline__ void combine8(const uint16_t *y, const float *w, cons
 #pragma unroll
     for (int q = 0; q < 8; q++) acc[q] += v[q];
   }
-  ((uint4 *)out)[(size_t)t * HC + c] = pack8(acc);
+  // the layer's output is not read again by the layer: stored non-temporally
+  st_once((uint4 *)out + (size_t)t * HC + c, pack8(acc));
 }
 
 }  // namespace moe
