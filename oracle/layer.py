@@ -164,21 +164,24 @@ def _swiglu_rows(Xhat, Wg, Wu, Wd, mx, R):
     return g, u, ahat, Y
 
 
-def expert_weights(w_gate, w_up, w_down, mx, backward=False):
+def expert_weights(w_gate, w_up, w_down, mx, backward=False, wfmt="e4m3"):
     """One expert's weights as one direction's GEMMs see them.
 
-    With MXFP8 every GEMM operand is quantised along that GEMM's contraction
-    axis.  The forward contracts gate/up ([H, I]) over H and down ([I, H])
-    over I: axis -2 of each.  The backward data gradients contract gate/up
-    over I (dX = dg W_gate^T) and down over H (dA = dY W_down^T): axis -1.
+    With MX operands every GEMM operand is quantised along that GEMM's
+    contraction axis.  The forward contracts gate/up ([H, I]) over H and down
+    ([I, H]) over I: axis -2 of each.  The backward data gradients contract
+    gate/up over I (dX = dg W_gate^T) and down over H (dA = dY W_down^T):
+    axis -1.  ``wfmt`` is the weights' element format: E4M3 (MXFP8
+    throughout), or a lower-precision one (FP4 E2M1, FP6 E2M3 / E3M2) for
+    lower-precision experts whose activations stay MXFP8.
     Returns dict(g, u, d) in fp64.
     """
     Wg, Wu, Wd = _val(w_gate), _val(w_up), _val(w_down)
     if not mx:
         return dict(g=Wg, u=Wu, d=Wd)
     ax = -1 if backward else -2
-    return dict(g=mx_roundtrip(Wg, axis=ax), u=mx_roundtrip(Wu, axis=ax),
-                d=mx_roundtrip(Wd, axis=ax))
+    return dict(g=mx_roundtrip(Wg, axis=ax, fmt=wfmt), u=mx_roundtrip(Wu, axis=ax, fmt=wfmt),
+                d=mx_roundtrip(Wd, axis=ax, fmt=wfmt))
 
 
 class ExpertWeights:
@@ -187,20 +190,22 @@ class ExpertWeights:
     memory at once.  ``fwd(e)`` / ``bwd(e)`` give dict(g, u, d) as the
     forward / backward data-gradient GEMMs see them."""
 
-    def __init__(self, inp, mx, shared=False):
+    def __init__(self, inp, mx, shared=False, wfmt="e4m3"):
         if shared:
             self.src = (inp["ws_gate"][None], inp["ws_up"][None], inp["ws_down"][None])
         else:
             self.src = (inp["w_gate"], inp["w_up"], inp["w_down"])
         self.mx = mx
+        self.wfmt = wfmt
         self.E = self.src[0].shape[0]
 
     def fwd(self, e):
-        return expert_weights(self.src[0][e], self.src[1][e], self.src[2][e], self.mx)
+        return expert_weights(self.src[0][e], self.src[1][e], self.src[2][e], self.mx,
+                              wfmt=self.wfmt)
 
     def bwd(self, e):
         return expert_weights(self.src[0][e], self.src[1][e], self.src[2][e], self.mx,
-                              backward=True)
+                              backward=True, wfmt=self.wfmt)
 
 
 THREADS = min(16, os.cpu_count() or 1)
@@ -224,7 +229,7 @@ def _each(fn, items):
 # Whole layer
 
 
-def forward(inp, k, mx=False, exact=False, routing=None, logits=None):
+def forward(inp, k, mx=False, exact=False, routing=None, logits=None, wfmt="e4m3"):
     """The layer's forward pass; returns every intermediate the backward needs.
 
     ``inp`` holds x, the expert weights and either a router (w_router, bias)
@@ -236,13 +241,15 @@ def forward(inp, k, mx=False, exact=False, routing=None, logits=None):
     implementation's logits here (the router backward still runs).
     ``routing`` (idx, w) overrides the router altogether (used by the
     exact-mode gradient tests, where the selection must stay fixed).
+    ``wfmt`` (with ``mx``) is the expert weights' MX element format (see
+    :func:`expert_weights`); the activations are MXFP8 either way.
     """
     if exact and mx:
         raise ValueError("exact mode has no quantiser")
     R = _Round(exact)
     x = _val(inp["x"])
     T, H = x.shape
-    W = ExpertWeights(inp, mx)
+    W = ExpertWeights(inp, mx, wfmt=wfmt)
     E = W.E
     I = inp["w_gate"].shape[2]
     if routing is not None:
@@ -271,14 +278,15 @@ def forward(inp, k, mx=False, exact=False, routing=None, logits=None):
         We = W.fwd(e)
         g[rs], u[rs], ahat[rs], Y[rs] = _swiglu_rows(Xhat[rs], We["g"], We["u"], We["d"], mx, R)
     _each(one, [e for e in range(E) if counts[e]])
-    WS = ExpertWeights(inp, mx, shared=True) if inp.get("ws_gate") is not None else None
+    WS = ExpertWeights(inp, mx, shared=True, wfmt=wfmt) if inp.get("ws_gate") is not None \
+        else None
     shared = None
     if WS is not None:
         Ws = WS.fwd(0)
         gs, us, as_, ys = _swiglu_rows(xhat_tok, Ws["g"], Ws["u"], Ws["d"], mx, R)
         shared = dict(g=gs, u=us, ahat=as_, y=ys)
     out = combine(Y, w, inv, k, None if shared is None else shared["y"], exact)
-    return dict(k=k, mx=mx, exact=exact, x=x, xhat_tok=xhat_tok, logits=logits,
+    return dict(k=k, mx=mx, wfmt=wfmt, exact=exact, x=x, xhat_tok=xhat_tok, logits=logits,
                 idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv,
                 Xhat=Xhat, g=g, u=u, ahat=ahat, Y=Y, shared=shared, out=out, W=W, WS=WS)
 
@@ -432,8 +440,8 @@ class _LazyWeights:
     ``keep`` most recently used experts: the sampled evaluators touch only a
     few experts."""
 
-    def __init__(self, inp, mx, shared=False, keep=16):
-        self.src = ExpertWeights(inp, mx, shared)
+    def __init__(self, inp, mx, shared=False, keep=16, wfmt="e4m3"):
+        self.src = ExpertWeights(inp, mx, shared, wfmt)
         self.keep = keep
         self.cache = {}
 
@@ -469,13 +477,13 @@ class TokenEvaluator:
     Rounding points and quantisation are those of :func:`forward`.
     """
 
-    def __init__(self, inp, k, mx=False):
+    def __init__(self, inp, k, mx=False, wfmt="e4m3"):
         self.inp, self.k, self.mx = inp, k, mx
         self.R = _Round(False)
         self.x = _val(inp["x"])
-        self.W = _LazyWeights(inp, mx)
-        self.WS = _LazyWeights(inp, mx, shared=True)[0] if inp.get("ws_gate") is not None \
-            else None
+        self.W = _LazyWeights(inp, mx, wfmt=wfmt)
+        self.WS = _LazyWeights(inp, mx, shared=True, wfmt=wfmt)[0] \
+            if inp.get("ws_gate") is not None else None
         if inp.get("topk_idx") is None:
             self.routing = None
         else:
@@ -537,7 +545,7 @@ class TokenEvaluator:
 
 
 def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, weights=None,
-                               logits=None):
+                               logits=None, wfmt="e4m3"):
     """dW_down[e, i, :], dW_gate[e, :, i], dW_up[e, :, i] for chosen columns i.
 
     Sums over the rows routed to expert e (found from the routing by
@@ -553,11 +561,11 @@ def expert_weight_grad_columns(inp, k, mx, e, cols, dout=None, shared=False, wei
     x = _val(inp["x"])
     dout = _val(inp["dout"] if dout is None else dout)
     if shared:
-        We = weights if weights is not None else _LazyWeights(inp, mx, shared=True)[0]
+        We = weights if weights is not None else _LazyWeights(inp, mx, True, wfmt=wfmt)[0]
         t = np.arange(x.shape[0])
         wrow = np.ones(x.shape[0])
     else:
-        We = weights if weights is not None else _LazyWeights(inp, mx)[e]
+        We = weights if weights is not None else _LazyWeights(inp, mx, wfmt=wfmt)[e]
         if logits is not None:
             idx, w = topk_softmax(logits, k)
         elif inp.get("topk_idx") is None:

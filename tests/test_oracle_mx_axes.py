@@ -19,19 +19,30 @@ import pytest
 
 import oracle
 from oracle import layer as L
-from oracle.mx import mx_roundtrip
+from oracle.mx import FORMATS, mx_roundtrip
 from oracle.numerics import bf16, bf16_to_f64, f32
 from synth import f32_to_bf16_bits
 
-TOP = 256.0 + 32.0 * np.arange(7)          # E4M3 values of exponent 8: 256 .. 448
-VALS = np.concatenate([np.ldexp(np.arange(1, 8), -9),      # subnormals
-                       np.ldexp(8.0 + np.arange(8), -3),   # normals in [1, 2)
-                       np.ldexp(8.0 + np.arange(8), 2)])   # normals in [32, 64)
+FMTS = ("e4m3", "e2m1", "e2m3", "e3m2")
 
 
-def representable(shape, axis, seed, s_lo=-14, s_hi=-9):
+def _levels(fmt):
+    """(values of the format's top binade, its other nonzero values, the
+    smallest ones included)."""
+    F = FORMATS[fmt]
+    mags = F.table[: F.ncodes // 2]
+    mags = mags[np.isfinite(mags) & (mags > 0)]
+    top = mags[np.floor(np.log2(mags)) == F.emax]
+    return top, mags[np.floor(np.log2(mags)) < F.emax]
+
+
+def representable(shape, axis, seed, s_lo=-14, s_hi=-9, fmt="e4m3"):
     """bf16 bits of a 2-D matrix whose 32-blocks along ``axis`` are exactly
-    representable in MXFP8, each with its own scale 2^s, s in [s_lo, s_hi]."""
+    representable in MX format ``fmt``, each with its own scale 2^s, s in
+    [s_lo, s_hi] (shifted by the format's emax relative to E4M3's)."""
+    TOP, VALS = _levels(fmt)
+    shift = 8 - FORMATS[fmt].emax
+    s_lo, s_hi = s_lo + shift, s_hi + shift
     rng = np.random.default_rng(seed)
     v = np.moveaxis(np.zeros(shape), axis, -1)
     nb = v.shape[-1] // 32
@@ -47,16 +58,20 @@ def representable(shape, axis, seed, s_lo=-14, s_hi=-9):
     return bits
 
 
-def _inputs(T, H, E, I, w_axis, seed):
+def _inputs(T, H, E, I, w_axis, seed, fmt="e4m3"):
     """A top-1 layer (weight 1.0 per token, so dY is dOut itself) whose x and
-    dOut rows are representable along H and whose expert weights are
-    representable along axis ``w_axis`` of each [rows, cols] matrix."""
+    dOut rows are representable along H in MXFP8 and whose expert weights are
+    representable in ``fmt`` along axis ``w_axis`` of each [rows, cols]
+    matrix."""
     rng = np.random.default_rng(seed)
+
+    def w(shape, sd):
+        return representable(shape, w_axis, sd, fmt=fmt)
     inp = dict(x=representable((T, H), 1, seed + 1, -8, -6),
                dout=representable((T, H), 1, seed + 2, -8, -6),
-               w_gate=np.stack([representable((H, I), w_axis, seed + 10 + e) for e in range(E)]),
-               w_up=np.stack([representable((H, I), w_axis, seed + 20 + e) for e in range(E)]),
-               w_down=np.stack([representable((I, H), w_axis, seed + 30 + e) for e in range(E)]),
+               w_gate=np.stack([w((H, I), seed + 10 + e) for e in range(E)]),
+               w_up=np.stack([w((H, I), seed + 20 + e) for e in range(E)]),
+               w_down=np.stack([w((I, H), seed + 30 + e) for e in range(E)]),
                topk_idx=rng.integers(E, size=(T, 1)).astype(np.int32),
                topk_w=np.ones((T, 1), np.float32))
     return inp
@@ -65,11 +80,11 @@ def _inputs(T, H, E, I, w_axis, seed):
 T, H, E, I = 96, 128, 3, 64
 
 
-def check_forward_axes(inp):
+def check_forward_axes(inp, fmt="e4m3"):
     """With weights representable along the forward contraction axis (-2),
     the MX forward's g, u are the unquantised products and Y is the product of
     its quantised activation with the raw W_down."""
-    fx = oracle.forward(inp, 1, mx=True)
+    fx = oracle.forward(inp, 1, mx=True, wfmt=fmt)
     fb = oracle.forward(inp, 1, mx=False)
     assert np.array_equal(fx["Xhat"], fb["Xhat"])           # x rows representable
     assert np.array_equal(fx["g"], fb["g"]), "gate weights quantised across H"
@@ -81,12 +96,12 @@ def check_forward_axes(inp):
             "down weights quantised across I"
 
 
-def check_backward_axes(inp):
+def check_backward_axes(inp, fmt="e4m3"):
     """With weights representable along the backward contraction axis (-1),
     the MX backward's dg, du equal those of the unquantised backward over the
     same forward state (dY = dOut is representable along H), and dX is the
     product of the quantised dg, du with the raw W_gate, W_up."""
-    fx = oracle.forward(inp, 1, mx=True)
+    fx = oracle.forward(inp, 1, mx=True, wfmt=fmt)
     bx = oracle.backward(inp, fx)
     fb = dict(fx, mx=False, W=L.ExpertWeights(inp, False))
     bb = oracle.backward(inp, fb)
@@ -101,18 +116,20 @@ def check_backward_axes(inp):
         assert np.array_equal(bx["dX"][rs], ref), "gate/up weights quantised across I"
 
 
-def test_construction_is_one_sided():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_construction_is_one_sided(fmt):
     for axis in (0, 1):
-        v = bf16_to_f64(representable((128, 64), axis, 3))
-        assert np.array_equal(mx_roundtrip(v, axis=axis), v)
-        assert not np.array_equal(mx_roundtrip(v, axis=1 - axis), v)
+        v = bf16_to_f64(representable((128, 64), axis, 3, fmt=fmt))
+        assert np.array_equal(mx_roundtrip(v, axis=axis, fmt=fmt), v)
+        assert not np.array_equal(mx_roundtrip(v, axis=1 - axis, fmt=fmt), v)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("backward", [False, True])
-def test_expert_weights_quantise_along_the_contraction_axis(backward):
+def test_expert_weights_quantise_along_the_contraction_axis(backward, fmt):
     axis = -1 if backward else -2
-    inp = _inputs(T, H, E, I, axis, seed=5)
-    W = L.ExpertWeights(inp, mx=True)
+    inp = _inputs(T, H, E, I, axis, seed=5, fmt=fmt)
+    W = L.ExpertWeights(inp, mx=True, wfmt=fmt)
     for e in range(E):
         got = W.bwd(e) if backward else W.fwd(e)
         other = W.fwd(e) if backward else W.bwd(e)
@@ -122,39 +139,42 @@ def test_expert_weights_quantise_along_the_contraction_axis(backward):
             assert not np.array_equal(other[key], raw), (key, e)
 
 
-def test_mx_forward_quantises_weights_along_h_for_gate_up_and_i_for_down():
-    check_forward_axes(_inputs(T, H, E, I, -2, seed=7))
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mx_forward_quantises_weights_along_h_for_gate_up_and_i_for_down(fmt):
+    check_forward_axes(_inputs(T, H, E, I, -2, seed=7, fmt=fmt), fmt)
 
 
-def test_mx_backward_quantises_weights_along_i_for_gate_up_and_h_for_down():
-    check_backward_axes(_inputs(T, H, E, I, -1, seed=9))
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mx_backward_quantises_weights_along_i_for_gate_up_and_h_for_down(fmt):
+    check_backward_axes(_inputs(T, H, E, I, -1, seed=9, fmt=fmt), fmt)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("which", ["gate", "up", "down"])
 @pytest.mark.parametrize("backward", [False, True])
-def test_swapped_axis_is_caught(monkeypatch, which, backward):
+def test_swapped_axis_is_caught(monkeypatch, which, backward, fmt):
     """Swap the axis of one weight in one direction: the matching check fails."""
     orig = L.expert_weights
     mutate_backward = backward
 
-    def mutant(w_gate, w_up, w_down, mx, backward=False):
-        W = orig(w_gate, w_up, w_down, mx, backward)
+    def mutant(w_gate, w_up, w_down, mx, backward=False, wfmt="e4m3"):
+        W = orig(w_gate, w_up, w_down, mx, backward, wfmt)
         bwd = backward
         if mx and bwd == mutate_backward:
             key = dict(gate="g", up="u", down="d")[which]
             raw = dict(g=w_gate, u=w_up, d=w_down)[key]
-            W[key] = mx_roundtrip(L._val(raw), axis=-2 if bwd else -1)
+            W[key] = mx_roundtrip(L._val(raw), axis=-2 if bwd else -1, fmt=wfmt)
         return W
 
     monkeypatch.setattr(L, "expert_weights", mutant)
     if backward:
-        inp = _inputs(T, H, E, I, -1, seed=9)
+        inp = _inputs(T, H, E, I, -1, seed=9, fmt=fmt)
         with pytest.raises(AssertionError):
-            check_backward_axes(inp)
+            check_backward_axes(inp, fmt)
     else:
-        inp = _inputs(T, H, E, I, -2, seed=7)
+        inp = _inputs(T, H, E, I, -2, seed=7, fmt=fmt)
         with pytest.raises(AssertionError):
-            check_forward_axes(inp)
+            check_forward_axes(inp, fmt)
 
 
 def test_exact_weights_give_f32_products():
