@@ -60,13 +60,32 @@ enum {
   MOE_ERR_DEVICE_TIMEOUT = 5 /* reported by moe_read_status only */
 };
 
-enum { MOE_BF16 = 0, MOE_MXFP8 = 1 };
+/* Datatypes of the layer.
+ * MOE_BF16: bf16 activations and weights, fp32 accumulation.
+ * MOE_MXFP8: every operand of the expert GEMMs in MXFP8 (E4M3 codes, one
+ *   E8M0 scale per 32 values along the contraction axis), quantised in the
+ *   dispatch and the SwiGLU epilogue [KC §02]; weights pre-quantised.
+ * MOE_MXFP8_W4, MOE_MXFP8_W6, MOE_MXFP8_W6E3M2: lower-precision experts --
+ *   the expert weights' MX copies in FP4 E2M1, FP6 E2M3 or FP6 E3M2 (one
+ *   E8M0 scale per 32 values, OCP MX conversion: nearest-even, saturating at
+ *   the format's maximum), the activations and gradients MXFP8 as above; the
+ *   pages mention 4-bit expert kernels (noticiai.com.br, "Por que a camada
+ *   MoE virou o gargalo").  FP4 weights take half the bytes of FP8 ones; FP6
+ *   blocks are stored in 32-byte slots (24 bytes of codes), so FP6 weights
+ *   take the bytes of FP8 ones. */
+enum {
+  MOE_BF16 = 0,
+  MOE_MXFP8 = 1,
+  MOE_MXFP8_W4 = 2,
+  MOE_MXFP8_W6 = 3,
+  MOE_MXFP8_W6E3M2 = 4
+};
 
 /* The layer's shape, following the quantities the pages tune the layer by:
  * hidden size, top-k and expert count [KC §03], expert intermediate size
  * [KC §02], plus the token count and the datatype.
  * Limits: 1 <= T; 1 <= k <= 16; 1 <= E <= 1024; H, I and shared_inter
- * multiples of 64 (of 128 for MXFP8); R = T*k < 2^31; H*E < 2^31. */
+ * multiples of 64 (of 128 for the MX types); R = T*k < 2^31; H*E < 2^31. */
 typedef struct moe_shape {
   int32_t tokens;       /* T */
   int32_t hidden;       /* H */
@@ -74,7 +93,7 @@ typedef struct moe_shape {
   int32_t top_k;        /* k */
   int32_t inter;        /* I */
   int32_t shared_inter; /* Is of the one shared expert; 0 = no shared expert */
-  int32_t dtype;        /* MOE_BF16 or MOE_MXFP8 */
+  int32_t dtype;        /* MOE_BF16, MOE_MXFP8 or a lower-precision-expert type */
 } moe_shape;
 
 /* How the layer's forward and backward are scheduled (moe_sched.schedule).
@@ -347,6 +366,37 @@ typedef struct moe_saved_view {
 
 int moe_saved_pointers(const moe_shape *shape, void *saved,
                        moe_saved_view *view);
+
+/* Device pointers into packed weights (host call, no device work): where
+ * moe_prepare_weights left the routed experts' MX copies (NULL for
+ * MOE_BF16).  Each copy is the weights laid out contraction-contiguous for
+ * one GEMM and quantised along that contraction axis, with E8M0 scales in
+ * the K-blocked layout of moe_dispatch:
+ *   gate_up  [E][2I][H]: gate and up interleaved in 32-row blocks (rows
+ *            64b .. 64b+31 = gate columns 32b .. 32b+31, the next 32 = up
+ *            columns), quantised along H (the forward gate/up GEMM);
+ *   down     [E][H][I] quantised along I (the forward down GEMM);
+ *   gate_up_t [E][H][2I] (the same interleave along 2I), quantised along 2I
+ *            (the gate/up data-gradient GEMM);
+ *   down_t   [E][I][H] quantised along H (the down data-gradient GEMM).
+ * Codes: one byte per value for E4M3; for FP6 each 32-value block takes 32
+ * bytes (24 bytes of 6-bit codes, value p at bits 6p.., then 8 zero bytes);
+ * for FP4 16 bytes (value p at bits 4p..), rows of half the values' count.
+ * fmt is the dtype's weight format: 0 E4M3, 2 FP6 E2M3, 3 FP6 E3M2,
+ * 4 FP4 E2M1. */
+typedef struct moe_packed_view {
+  uint8_t *gate_up;
+  uint8_t *gate_up_scale;
+  uint8_t *down;
+  uint8_t *down_scale;
+  uint8_t *gate_up_t;
+  uint8_t *gate_up_t_scale;
+  uint8_t *down_t;
+  uint8_t *down_t_scale;
+  int32_t fmt;
+} moe_packed_view;
+
+int moe_packed_pointers(const moe_shape *shape, void *packed, moe_packed_view *view);
 
 /* Device pointers into a workspace (host call, no device work): where the
  * last call that used `ws` left its intermediates, for callers that inspect

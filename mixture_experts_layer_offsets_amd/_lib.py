@@ -22,6 +22,12 @@ MOE_ERR_HIP = 4
 MOE_ERR_DEVICE_TIMEOUT = 5
 MOE_BF16 = 0
 MOE_MXFP8 = 1
+MOE_MXFP8_W4 = 2        # MXFP8 activations, FP4 E2M1 expert weights
+MOE_MXFP8_W6 = 3        # MXFP8 activations, FP6 E2M3 expert weights
+MOE_MXFP8_W6E3M2 = 4    # MXFP8 activations, FP6 E3M2 expert weights
+# expert-weight element format of each MX datatype (the oracle's names)
+WEIGHT_FORMAT = {MOE_MXFP8: "e4m3", MOE_MXFP8_W4: "e2m1", MOE_MXFP8_W6: "e2m3",
+                 MOE_MXFP8_W6E3M2: "e3m2"}
 MOE_SCHED_STAGED = 0
 MOE_SCHED_PERSISTENT = 1
 MOE_SCHED_PIPELINED = 2
@@ -72,6 +78,7 @@ SIGNATURES = {
     "moe_layer_bwd": (c_int, [c_void_p] * 14 + [c_void_p, c_size_t, c_void_p]),
     "moe_decode_fwd": (c_int, [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]),
     "moe_saved_pointers": (c_int, [c_void_p, c_void_p, c_void_p]),
+    "moe_packed_pointers": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_workspace_pointers": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_read_status": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_strerror": (ctypes.c_char_p, [c_int]),
@@ -235,6 +242,19 @@ def moe_saved_pointers(shape, saved) -> dict:
     _ck(load().moe_saved_pointers(_shape(shape), _p(saved), ctypes.byref(view)),
         "moe_saved_pointers")
     return {n: getattr(view, n) for n, _ in MoeSavedView._fields_}
+
+
+class MoePackedView(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in (
+        "gate_up", "gate_up_scale", "down", "down_scale", "gate_up_t", "gate_up_t_scale",
+        "down_t", "down_t_scale")] + [("fmt", ctypes.c_int32)]
+
+
+def moe_packed_pointers(shape, packed) -> dict:
+    view = MoePackedView()
+    _ck(load().moe_packed_pointers(_shape(shape), _p(packed), ctypes.byref(view)),
+        "moe_packed_pointers")
+    return {n: getattr(view, n) for n, _ in MoePackedView._fields_}
 
 
 class MoeWorkView(ctypes.Structure):

@@ -52,6 +52,7 @@ struct Carver {
 struct Dims {
   long T, H, E, k, I, Is, R;
   bool mx, shared;
+  int wfmt;  // element format of the expert weights' MX copies (kMx*)
 };
 
 int check_shape(const moe_shape *s, Dims *d) {
@@ -59,16 +60,20 @@ int check_shape(const moe_shape *s, Dims *d) {
   if (s->tokens < 1 || s->hidden < 1 || s->experts < 1 || s->top_k < 1 || s->inter < 1 ||
       s->shared_inter < 0)
     return MOE_ERR_INVALID_ARG;
-  if (s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (s->dtype < MOE_BF16 || s->dtype > MOE_MXFP8_W6E3M2) return MOE_ERR_INVALID_ARG;
   const long R = (long)s->tokens * s->top_k;
   if (R >= (1L << 31)) return MOE_ERR_INVALID_ARG;
-  const int mult = s->dtype == MOE_MXFP8 ? 128 : 64;
+  const int mult = s->dtype != MOE_BF16 ? 128 : 64;
   if (s->hidden % mult || s->inter % mult || s->shared_inter % mult) return MOE_ERR_UNSUPPORTED;
   if (s->experts > 1024 || s->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)s->hidden * s->experts >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
   d->T = s->tokens; d->H = s->hidden; d->E = s->experts; d->k = s->top_k; d->I = s->inter;
-  d->Is = s->shared_inter; d->R = R; d->mx = s->dtype == MOE_MXFP8;
+  d->Is = s->shared_inter; d->R = R; d->mx = s->dtype != MOE_BF16;
   d->shared = s->shared_inter > 0;
+  d->wfmt = s->dtype == MOE_MXFP8_W4     ? kMxE2M1
+            : s->dtype == MOE_MXFP8_W6   ? kMxE2M3
+            : s->dtype == MOE_MXFP8_W6E3M2 ? kMxE3M2
+                                         : kMxE4M3;
   return MOE_OK;
 }
 
@@ -243,7 +248,8 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
 // ---- packed weights: one expert set (routed: G = E; shared: G = 1)
 struct WSet {
   uint16_t *guT, *dT, *gu, *d;  // bf16: [G][2I][H], [G][H][I], [G][H][2I], [G][I][H]
-  MxT guTq, dTq, guq, dq;       // MXFP8 copies, each quantised along its contraction axis
+  MxT guTq, dTq, guq, dq;       // MX copies, each quantised along its contraction axis
+  int fmt = kMxE4M3;            // their element format (E2M1: rows of half the bytes)
 };
 
 WSet take_wset(Carver &c, long G, long H, long I, bool mx) {
@@ -269,7 +275,11 @@ size_t carve_packed(const Dims &d, const void *base, Packed *p) {
   Carver c((void *)base);
   Packed t{};
   t.r = take_wset(c, d.E, d.H, d.I, d.mx);
-  if (d.shared) t.s = take_wset(c, 1, d.H, d.Is, d.mx);
+  t.r.fmt = d.wfmt;
+  if (d.shared) {
+    t.s = take_wset(c, 1, d.H, d.Is, d.mx);
+    t.s.fmt = d.wfmt;
+  }
   if (p) *p = t;
   return c.off;
 }
@@ -304,11 +314,26 @@ void pack_wset(const WSet &w, int G, int H, int I, const uint16_t *wg, const uin
   launch_interleave_copy(wg, w.gu, G, H, I, 2 * I, 64, 0, s);
   launch_interleave_copy(wu, w.gu, G, H, I, 2 * I, 64, 32, s);
   launch_interleave_copy(wd, w.d, G, I, H, H, 32, 0, s);  // plain copy, [G][I][H]
-  if (mx) {
+  if (mx && w.fmt == kMxE4M3) {
     launch_quant_rows_mx(w.guT, G * 2 * I, H, w.guTq.q, w.guTq.s, s);  // along H
     launch_quant_rows_mx(w.dT, G * H, I, w.dTq.q, w.dTq.s, s);         // along I
     launch_quant_rows_mx(w.gu, G * H, 2 * I, w.guq.q, w.guq.s, s);     // along I
     launch_quant_rows_mx(w.d, G * I, H, w.dq.q, w.dq.s, s);            // along H
+  } else if (mx) {
+    launch_quant_rows_mx_low(w.guT, G * 2 * I, H, w.guTq.q, w.guTq.s, w.fmt, s);
+    launch_quant_rows_mx_low(w.dT, G * H, I, w.dTq.q, w.dTq.s, w.fmt, s);
+    launch_quant_rows_mx_low(w.gu, G * H, 2 * I, w.guq.q, w.guq.s, w.fmt, s);
+    launch_quant_rows_mx_low(w.d, G * I, H, w.dq.q, w.dq.s, w.fmt, s);
+  }
+}
+
+// The weights' MX codes as a GEMM's B operand: E2M1 codes take half a byte
+// per value, so the row pitch and the per-expert stride (set in values, as
+// for one-byte E4M3 and the 32-byte-slot FP6 rows) halve.
+void weight_pitch(const WSet &W, GemmArgs *p) {
+  if (W.fmt == kMxE2M1) {
+    p->ldb /= 2;
+    p->sB /= 2;
   }
 }
 
@@ -332,7 +357,8 @@ void gemm_gate_up(const uint16_t *x, MxT xq, const int32_t *offsets, const int32
     launch_gemm_rows(p, EPI_SWIGLU, true, (int)grid_rows, s);
   } else {
     p.A = (const uint16_t *)xq.q; p.B = (const uint16_t *)W.guTq.q;
-    const MxOperands m{xq.s, W.guTq.s, (int)a_rows, aq.q, aq.s};
+    const MxOperands m{xq.s, W.guTq.s, (int)a_rows, aq.q, aq.s, W.fmt};
+    weight_pitch(W, &p);
     launch_gemm_rows_mx(p, m, EPI_SWIGLU, (int)grid_rows, s);
   }
 }
@@ -350,7 +376,8 @@ void gemm_down(const uint16_t *act, MxT aq, const int32_t *offsets, const int32_
     launch_gemm_rows(q, EPI_BF16, true, (int)grid_rows, s);
   } else {
     q.A = (const uint16_t *)aq.q; q.B = (const uint16_t *)W.dTq.q;
-    const MxOperands m{aq.s, W.dTq.s, (int)a_rows, nullptr, nullptr};
+    const MxOperands m{aq.s, W.dTq.s, (int)a_rows, nullptr, nullptr, W.fmt};
+    weight_pitch(W, &q);
     launch_gemm_rows_mx(q, m, EPI_BF16, (int)grid_rows, s);
   }
 }
@@ -385,7 +412,8 @@ void gemm_dgrad_down(const uint16_t *dY, MxT dyq, const int32_t *offsets, const 
     launch_gemm_rows(a, EPI_SWIGLU_BWD, true, (int)grid_rows, s);
   } else {
     a.A = (const uint16_t *)dyq.q; a.B = (const uint16_t *)W.dq.q;
-    const MxOperands m{dyq.s, W.dq.s, (int)a_rows, nullptr, nullptr};
+    const MxOperands m{dyq.s, W.dq.s, (int)a_rows, nullptr, nullptr, W.fmt};
+    weight_pitch(W, &a);
     launch_gemm_rows_mx(a, m, EPI_SWIGLU_BWD, (int)grid_rows, s);
   }
 }
@@ -403,7 +431,8 @@ void gemm_dgrad_gate_up(const uint16_t *dh, MxT dhq, const int32_t *offsets, con
     launch_gemm_rows(c, EPI_BF16, true, (int)grid_rows, s);
   } else {
     c.A = (const uint16_t *)dhq.q; c.B = (const uint16_t *)W.guq.q;
-    const MxOperands m{dhq.s, W.guq.s, (int)a_rows, nullptr, nullptr};
+    const MxOperands m{dhq.s, W.guq.s, (int)a_rows, nullptr, nullptr, W.fmt};
+    weight_pitch(W, &c);
     launch_gemm_rows_mx(c, m, EPI_BF16, (int)grid_rows, s);
   }
 }
@@ -1360,6 +1389,24 @@ int moe_decode_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_
   }
   launch_combine(w.dX, wts, w.dec_inv, d.shared ? w.dxs : nullptr, out, T, k, H, s);
   return hip_status();
+}
+
+int moe_packed_pointers(const moe_shape *shape, void *packed, moe_packed_view *view) {
+  if (!view) return MOE_ERR_INVALID_ARG;
+  *view = moe_packed_view{};
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!packed) return MOE_ERR_INVALID_ARG;
+  Packed p;
+  carve_packed(d, packed, &p);
+  view->fmt = d.wfmt;
+  if (!d.mx) return MOE_OK;
+  view->gate_up = p.r.guTq.q; view->gate_up_scale = p.r.guTq.s;
+  view->down = p.r.dTq.q; view->down_scale = p.r.dTq.s;
+  view->gate_up_t = p.r.guq.q; view->gate_up_t_scale = p.r.guq.s;
+  view->down_t = p.r.dq.q; view->down_t_scale = p.r.dq.s;
+  return MOE_OK;
 }
 
 int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view) {

@@ -6,7 +6,7 @@
 
 namespace moe {
 
-template <int EPI>
+template <int EPI, int BFMT>
 __global__ __launch_bounds__(NT, 1) void gemm_mx_kernel(GemmArgs p, MxOperands mx) {
   __shared__ __attribute__((aligned(1024))) uint8_t L0[2 * BM * MXK];  // [A | B], even stages
   __shared__ __attribute__((aligned(1024))) uint8_t L1[2 * BM * MXK];  // [A | B], odd stages
@@ -22,8 +22,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_mx_kernel(GemmArgs p, MxOperands m
   }
   const int g = lo;
   const int rowbase = p.offsets[g];
-  mx_tile<EPI>(p, mx, g, (mt - p.tile_start[g]) * BM, nt * BN, rowbase,
-               p.offsets[g + 1] - rowbase, L0, L1);
+  mx_tile<EPI, BFMT>(p, mx, g, (mt - p.tile_start[g]) * BM, nt * BN, rowbase,
+                     p.offsets[g + 1] - rowbase, L0, L1);
+}
+
+template <int BFMT>
+static void launch_mx_fmt(const GemmArgs &p, const MxOperands &mx, int epi, const dim3 &gr,
+                          hipStream_t s) {
+  const dim3 b(NT);
+  switch (epi) {
+    case EPI_BF16:
+      hipLaunchKernelGGL((gemm_mx_kernel<EPI_BF16, BFMT>), gr, b, 0, s, p, mx);
+      break;
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL((gemm_mx_kernel<EPI_SWIGLU, BFMT>), gr, b, 0, s, p, mx);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_mx_kernel<EPI_SWIGLU_BWD, BFMT>), gr, b, 0, s, p, mx);
+      break;
+  }
 }
 
 void launch_gemm_rows_mx(const GemmArgs &p0, const MxOperands &mx, int epi, int max_rows,
@@ -32,12 +49,82 @@ void launch_gemm_rows_mx(const GemmArgs &p0, const MxOperands &mx, int epi, int 
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long grid = ((long)max_rows / BM + p.G) * p.n_tiles_n;
   if (grid <= 0) return;
-  const dim3 gr((unsigned)grid), b(NT);
-  switch (epi) {
-    case EPI_BF16: hipLaunchKernelGGL(gemm_mx_kernel<EPI_BF16>, gr, b, 0, s, p, mx); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_mx_kernel<EPI_SWIGLU>, gr, b, 0, s, p, mx); break;
-    default: hipLaunchKernelGGL(gemm_mx_kernel<EPI_SWIGLU_BWD>, gr, b, 0, s, p, mx); break;
+  const dim3 gr((unsigned)grid);
+  switch (mx.b_fmt) {
+    case kMxE2M1: launch_mx_fmt<kMxE2M1>(p, mx, epi, gr, s); break;
+    case kMxE2M3: launch_mx_fmt<kMxE2M3>(p, mx, epi, gr, s); break;
+    case kMxE3M2: launch_mx_fmt<kMxE3M2>(p, mx, epi, gr, s); break;
+    default: launch_mx_fmt<kMxE4M3>(p, mx, epi, gr, s); break;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Lower-precision MX copies of the expert weights.  One thread per 32-value
+// block of a row: s = clamp(floor(log2 amax) - emax, -127, 127) (an all-zero
+// block: -127), each value clamped to the format's maximum at scale 2^s and
+// rounded to nearest, ties to even, with gradual underflow below the
+// smallest normal 2^emin: with e = max(floor(log2 |v|), emin) the code's
+// magnitude bits are 2^m (e - emin) + rint(|v| 2^(m - e)), and the sign bit
+// is set exactly when v < 0.  Formats: E2M1 (m 1, emin 0, emax 2, max 6),
+// E2M3 (m 3, emin 0, emax 2, max 7.5), E3M2 (m 2, emin -2, emax 4, max 28).
+
+struct LowFmt {
+  int m, emin, emax, sign_shift;
+  float vmax;
+};
+
+__device__ __forceinline__ uint32_t low_encode(float v, const LowFmt &f) {
+  const float a = fminf(fabsf(v), f.vmax);
+  const int e = a < ldexpf(1.0f, f.emin) ? f.emin : floor_log2(a);
+  const uint32_t q = (uint32_t)rintf(ldexpf(a, f.m - e));
+  return (((uint32_t)(e - f.emin)) << f.m) + q + (v < 0.0f ? (1u << f.sign_shift) : 0u);
+}
+
+__global__ __launch_bounds__(256) void quant_rows_low_kernel(const uint16_t *__restrict__ src,
+                                                             int rows, int K,
+                                                             uint8_t *__restrict__ q,
+                                                             uint8_t *__restrict__ sc, int fmt) {
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  const int nb = K / 32;
+  if (id >= (long)rows * nb) return;
+  const int r = (int)(id / nb), blk = (int)(id - (long)r * nb);
+  const LowFmt f = fmt == kMxE2M1   ? LowFmt{1, 0, 2, 3, 6.0f}
+                   : fmt == kMxE2M3 ? LowFmt{3, 0, 2, 5, 7.5f}
+                                    : LowFmt{2, -2, 4, 5, 28.0f};
+  float v[32];
+  const uint4 *p4 = (const uint4 *)(src + (size_t)r * K + blk * 32);
+#pragma unroll
+  for (int i = 0; i < 4; i++) unpack8(p4[i], v + 8 * i);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+  int s = -127;
+  if (amax > 0.0f) s = max(-127, min(127, floor_log2(amax) - f.emax));
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int width = fmt == kMxE2M1 ? 4 : 6;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    const unsigned long long c = low_encode(ldexpf(v[i], -s), f);
+    const int bit = width * i;
+    w[bit >> 5] |= (uint32_t)(c << (bit & 31));
+    if ((bit & 31) + width > 32) w[(bit >> 5) + 1] |= (uint32_t)(c >> (32 - (bit & 31)));
+  }
+  if (fmt == kMxE2M1) {
+    *(uint4 *)(q + (size_t)r * (K / 2) + blk * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint4 *d = (uint4 *)(q + (size_t)r * K + blk * 32);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], 0u, 0u);
+  }
+  sc[((size_t)(blk >> 2) * rows + r) * 4 + (blk & 3)] = (uint8_t)(s + 127);
+}
+
+void launch_quant_rows_mx_low(const uint16_t *src, int rows, int K, uint8_t *q, uint8_t *sc,
+                              int fmt, hipStream_t s) {
+  const long n = (long)rows * (K / 32);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(quant_rows_low_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     src, rows, K, q, sc, fmt);
 }
 
 // ---------------------------------------------------------------------------

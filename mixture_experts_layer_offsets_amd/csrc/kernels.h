@@ -135,13 +135,26 @@ void launch_gemm_rows(const GemmArgs &p, int epi, bool b_kcontig, int max_rows, 
 // row r and 32-wide block b is byte (b/4 * rows + r) * 4 + b%4, i.e.
 // [K/128][rows][4].  A GEMM stage (128 values of K) then finds the scales of
 // a tile's consecutive rows in consecutive dwords.
+// Element formats of an MX GEMM's B operand (the expert weights), as the
+// f8f6f4 matrix instruction numbers them: E4M3 (MXFP8), FP6 E2M3, FP6 E3M2,
+// FP4 E2M1.  A operands (activations, gradients) are always E4M3.
+constexpr int kMxE4M3 = 0, kMxE2M3 = 2, kMxE3M2 = 3, kMxE2M1 = 4;
+
 struct MxOperands {
   const uint8_t *a_scale;   // A scales, [K/128][a_rows][4]
   const uint8_t *b_scale;   // B scales, [K/128][G*N][4] (row g*N + n)
   int a_rows;               // rows of the A scale matrix
   uint8_t *q_out;           // SwiGLU MX epilogue: a codes [rows][I]
   uint8_t *s_out;           // SwiGLU MX epilogue: a scales, [I/128][a_rows][4]
+  int b_fmt = kMxE4M3;      // B element format (kMx*); E2M1 rows are K/2 bytes
 };
+
+// MX codes of a bf16 matrix [rows][K] quantised along K in a lower-precision
+// element format (kMxE2M3, kMxE3M2, kMxE2M1), with the E8M0 scales K-blocked
+// as for E4M3.  E2M1: 16 bytes per 32-value block, rows of K/2 bytes; FP6:
+// 24 bytes of codes and 8 zero bytes per block, rows of K bytes.
+void launch_quant_rows_mx_low(const uint16_t *src, int rows, int K, uint8_t *q, uint8_t *sc,
+                              int fmt, hipStream_t s);
 void launch_gemm_rows_mx(const GemmArgs &p, const MxOperands &mx, int epi, int max_rows,
                          hipStream_t s);
 

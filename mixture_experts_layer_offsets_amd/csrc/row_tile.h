@@ -177,10 +177,25 @@ constexpr int MXK = 128;  // K bytes (= fp8 values) per stage
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// The MXFP8 tile; same geometry and buffers as nt_tile.
-template <int EPI>
+// Lower-precision B operands (the expert weights of the lower-precision
+// variants; A stays E4M3).  Measured on MI355X for the f8f6f4 instruction
+// with an FP4 or FP6 B operand: lane l supplies column l & 31, and lane half
+// h the 32 consecutive K values of block h, packed little-endian (value p at
+// bits [W p, W p + W), W = 4 or 6): 16 bytes per block for FP4, 24 for FP6.
+// FP4 rows are stored packed (64 bytes per 128-value stage, four 16-byte
+// chunks, swizzled within the row by swz4); FP6 blocks sit in 32-byte slots
+// (24 bytes of codes, 8 of zeros) so an FP6 row has the FP8 row's geometry.
+// BFMT is the instruction's B format code: 0 E4M3, 2 FP6 E2M3, 3 FP6 E3M2,
+// 4 FP4 E2M1.
+__device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 2)) & 3; }
+
+// The MX tile; same geometry and buffers as nt_tile.
+template <int EPI, int BFMT = kMxE4M3>
 __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx, int g, int m0,
                                         int n0, int rowbase, int Mg, uint8_t *L0, uint8_t *L1) {
+  // B bytes per row and stage, and B DMA instructions per wave and stage
+  constexpr int BKB = BFMT == kMxE2M1 ? MXK / 2 : MXK;
+  constexpr int NBQ = BFMT == kMxE2M1 ? 4 : 8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
@@ -208,7 +223,13 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
     const int kc = (lane & 7) ^ swz5(row);
     oa[i] = (uint32_t)(row * (int)p.lda + kc * 16);
-    ob[i] = (uint32_t)(row * (int)p.ldb + kc * 16);
+    if constexpr (BFMT == kMxE2M1) {
+      // 16 rows of four 16-byte chunks per instruction
+      const int rb = (wave * 4 + (i & 3)) * 16 + (lane >> 2);
+      ob[i] = (uint32_t)(rb * (int)p.ldb + (((lane & 3) ^ swz4(rb)) * 16));
+    } else {
+      ob[i] = (uint32_t)(row * (int)p.ldb + kc * 16);
+    }
   }
   // A stage index past the end selects empty descriptors: the DMA then writes
   // zeros into the (no longer read) buffer and touches no memory.  This keeps
@@ -216,7 +237,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   // MFMAs of a k-slice past the barrier and collapse the pipeline.
   const __amdgpu_buffer_rsrc_t rNone =
       __builtin_amdgcn_make_buffer_rsrc((void *)Ac, (short)0, 0, kBufferDword3);
-  // DMA instruction q (0-7: A rows, 8-15: B rows) of stage kt into L.
+  // DMA instruction q (0-7: A rows, 8 .. 8+NBQ-1: B rows) of stage kt into L.
   auto dma = [&](uint8_t *L, int kt, int q) {
     const bool live = kt < K / MXK;
     const int soff = live ? kt * MXK : 0;
@@ -224,14 +245,14 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone,
                                                (lds_ptr_t)(L + (wave * 8 + q) * 1024), 16, oa[q],
                                                soff, 0, 0);
-    else
+    else if (q < 8 + NBQ)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          live ? rB : rNone, (lds_ptr_t)(L + BM * MXK + (wave * 8 + q - 8) * 1024), 16,
-          ob[q - 8], soff, 0, 0);
+          live ? rB : rNone, (lds_ptr_t)(L + BM * MXK + (wave * NBQ + q - 8) * 1024), 16,
+          ob[q - 8], BKB == MXK ? soff : soff / 2, 0, 0);
   };
   auto issue = [&](uint8_t *L, int kt) {
 #pragma unroll
-    for (int q = 0; q < 16; q++) dma(L, kt, q);
+    for (int q = 0; q < 8 + NBQ; q++) dma(L, kt, q);
   };
   // scale dwords of this lane's rows (4 blocks of 32 along K per stage); 32
   // consecutive rows' dwords are one 128-byte line
@@ -253,7 +274,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
     for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
 
   const int sw = swz5(fr);
-  const int baseA = (wm0 + fr) * MXK, baseB = BM * MXK + (wn0 + fr) * MXK;
+  const int baseA = (wm0 + fr) * MXK, baseB = BM * MXK + (wn0 + fr) * BKB;
   // Same pipeline as nt_tile, with two 64-deep k-slices per stage: slice 1's
   // fragments load while slice 0's MFMAs run, then the wait and the barrier,
   // then the next stage's slice-0 fragments load while slice 1's MFMAs run.
@@ -268,16 +289,31 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
       const uint4 x1 = *(const uint4 *)(L + baseA + i * 32 * MXK + c1);
       fa[set][i] = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                            (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      const uint4 y0 = *(const uint4 *)(L + baseB + i * 32 * MXK + c0);
-      const uint4 y1 = *(const uint4 *)(L + baseB + i * 32 * MXK + c1);
-      fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
-                           (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+      if constexpr (BFMT == kMxE4M3) {
+        const uint4 y0 = *(const uint4 *)(L + baseB + i * 32 * BKB + c0);
+        const uint4 y1 = *(const uint4 *)(L + baseB + i * 32 * BKB + c1);
+        fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                             (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+      } else if constexpr (BFMT == kMxE2M1) {
+        // block 2ks + h: one 16-byte chunk
+        const uint4 y0 =
+            *(const uint4 *)(L + baseB + i * 32 * BKB + (((2 * ks + h) ^ swz4(fr)) << 4));
+        fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, 0, 0, 0, 0};
+      } else {
+        // block 2ks + h: the 32-byte slot's two chunks (24 bytes of codes)
+        const int b2 = 2 * (2 * ks + h);
+        const uint4 y0 = *(const uint4 *)(L + baseB + i * 32 * BKB + ((b2 ^ sw) << 4));
+        const uint4 y1 = *(const uint4 *)(L + baseB + i * 32 * BKB + (((b2 + 1) ^ sw) << 4));
+        fb[set][i] = (i32x8){(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                             (int)y1.x, (int)y1.y, 0, 0};
+      }
     }
   };
   auto mma1 = [&](int ks, int i, int j, const int *sa, const int *sb) {
     const int sh = 8 * (2 * ks + h);
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0, (sa[i] >> sh) & 0xFF, 0, (sb[j] >> sh) & 0xFF);
+        fa[ks][i], fb[ks][j], acc[i][j], 0, BFMT, 0, (sa[i] >> sh) & 0xFF, 0,
+        (sb[j] >> sh) & 0xFF);
   };
   auto mma = [&](int ks, const int *sa, const int *sb) {
 #pragma unroll

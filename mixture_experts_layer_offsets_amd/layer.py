@@ -99,5 +99,17 @@ class MoeLayer:
         nbytes = n * torch.empty((), dtype=dtype).element_size()
         return self.ws[off:off + nbytes].view(dtype).view(*shape)
 
+    def packed_tensor(self, name: str, shape) -> torch.Tensor:
+        """A uint8 view of one of the packed weights' MX copies or scale
+        planes (moe_packed_pointers), e.g. "gate_up" or "down_t_scale"."""
+        ptr = _lib.moe_packed_pointers(self.shape, self.packed)[name]
+        if not ptr:
+            raise KeyError(name)
+        off = ptr - self.packed.data_ptr()
+        n = 1
+        for d in shape:
+            n *= d
+        return self.packed[off:off + n].view(*shape)
+
     def status(self) -> int:
         return _lib.moe_read_status(self.ws)

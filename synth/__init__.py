@@ -49,6 +49,8 @@ class Workload:
     k: int                      # top-k
     I: int                      # expert intermediate size
     mx: bool = False            # MXFP8 (E4M3 + E8M0 per 32-element block)
+    wfmt: str = "e4m3"          # with mx: the expert weights' MX element format
+                                # (e4m3, or e2m1 / e2m3 / e3m2 for lower-precision experts)
     routing: str = "router"     # "router" (W_r given) or "supplied" (idx, w given)
     router_std: float = 0.0     # std of W_r entries (router routing)
     zipf_s: float = 0.0         # Zipf exponent of supplied routing (0 = uniform)

@@ -65,8 +65,16 @@ def note(msg: str):
     sys.stdout.flush()
 
 
-def shape_of(w, dtype=m.MOE_BF16):
-    return m.Shape(w.T, w.H, w.E, w.k, w.I, w.shared_I, dtype)
+def dtype_of(w):
+    """The library datatype of workload ``w``."""
+    if not w.mx:
+        return m.MOE_BF16
+    return {"e4m3": m.MOE_MXFP8, "e2m1": m.MOE_MXFP8_W4, "e2m3": m.MOE_MXFP8_W6,
+            "e3m2": m.MOE_MXFP8_W6E3M2}[w.wfmt]
+
+
+def shape_of(w, dtype=None):
+    return m.Shape(w.T, w.H, w.E, w.k, w.I, w.shared_I, dtype_of(w) if dtype is None else dtype)
 
 
 class Run:
@@ -77,7 +85,7 @@ class Run:
         self.w = w
         self.inp = inp if inp is not None else __import__("synth").make_inputs(w)
         inp = self.inp
-        self.shape = shape_of(w, m.MOE_MXFP8 if w.mx else m.MOE_BF16)
+        self.shape = shape_of(w)
         self.layer = m.MoeLayer(self.shape)
         self.layer.prepare(dev(inp["w_gate"]), dev(inp["w_up"]), dev(inp["w_down"]),
                            dev(inp["ws_gate"]), dev(inp["ws_up"]), dev(inp["ws_down"]))
@@ -111,10 +119,10 @@ def oracle_forward(inp, w, logits_gpu=None, mx=None):
     """
     mx = w.mx if mx is None else mx
     if w.routing != "router":
-        return oracle.forward(inp, w.k, mx=mx)
+        return oracle.forward(inp, w.k, mx=mx, wfmt=w.wfmt)
     own = oracle.router_logits(inp["x"], inp["w_router"], inp.get("bias"))
     check_rel("logits", logits_gpu, own, 1e-4)
-    fw = oracle.forward(inp, w.k, mx=mx, logits=logits_gpu)
+    fw = oracle.forward(inp, w.k, mx=mx, logits=logits_gpu, wfmt=w.wfmt)
     own_idx, _ = oracle.topk_softmax(own, w.k)
     n = int(np.any(own_idx != fw["idx"], axis=1).sum())
     note(f"  routing from the GPU's logits; {n} of {w.T} tokens would route differently "

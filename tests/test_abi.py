@@ -66,7 +66,8 @@ def test_struct_layouts_match_header():
     text = open(HEADER).read()
     for cname, pyt in (("moe_shape", _lib.MoeShape), ("moe_sched", _lib.MoeSched),
                        ("moe_saved_view", _lib.MoeSavedView),
-                       ("moe_work_view", _lib.MoeWorkView)):
+                       ("moe_work_view", _lib.MoeWorkView),
+                       ("moe_packed_view", _lib.MoePackedView)):
         body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (cname, cname), text, re.S).group(1)
         body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
         fields = []
