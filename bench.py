@@ -48,7 +48,7 @@ MX_GEMMS = ("gemm_gate_up_swiglu", "gemm_down", "gemm_dgrad_down_swiglu_bwd",
 CSRC = os.path.join(ROOT, "mixture_experts_layer_offsets_amd", "csrc")
 KERNEL_SOURCES = {
     "gemm_nt_kernel<2>": ("gemm.hip", "gemm_common.h", "row_tile.h", "tile_epilogue.h"),
-    "gemm_mx_kernel<2>": ("gemm_mx.hip", "gemm_common.h", "mx_device.h", "row_tile.h",
+    "gemm_mx_kernel<2, 0>": ("gemm_mx.hip", "gemm_common.h", "mx_device.h", "row_tile.h",
                           "tile_epilogue.h"),
 }
 
@@ -311,7 +311,7 @@ class Bench:
                         # leaves dirty lines the timed stage would have to
                         # write back)
                         flush.fill_(stage)
-                        flush.view(torch.int32).sum()
+                        flush.view(torch.int64).sum()  # a plain read, no widening copy
                 return _lib.STAGE_HOOK(fn)
             from mixture_experts_layer_offsets_amd import _lib
             hooks = (mk(FLUSH_FWD), mk(FLUSH_BWD))
@@ -379,7 +379,7 @@ class Bench:
                       for k in byts if k in stage_ms and stage_ms[k] > 0}
         dom = "gemm_gate_up_swiglu"
         achieved = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
-        kernel = "gemm_mx_kernel<2>" if w.mx else "gemm_nt_kernel<2>"
+        kernel = "gemm_mx_kernel<2, 0>" if w.mx else "gemm_nt_kernel<2>"
         res = {
             "value": w.T * a.steps / elapsed,
             "ms_per_step": elapsed / a.steps * 1e3,
