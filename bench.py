@@ -146,6 +146,14 @@ def sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
+def _dtype_name(w, mx_wgrad=False) -> str:
+    """The arithmetic the expert GEMMs run in."""
+    if not w.mx:
+        return "bf16"
+    s = "mxfp8" if w.wfmt == "e4m3" else f"mxfp8 activations x {w.wfmt} MX weights"
+    return s + " (weight gradients too)" if mx_wgrad else s
+
+
 def _traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on this workload and the current kernel sources; else None."""
@@ -234,8 +242,8 @@ class Bench:
                 x = x.view(np.int16)
             return torch.from_numpy(x).to(dev)
         self.d = d
-        shape = m.Shape(w.T, w.H, w.E, w.k, w.I, w.shared_I,
-                        m.MOE_MXFP8 if w.mx else m.MOE_BF16)
+        dtype = {v: k for k, v in m.WEIGHT_FORMAT.items()}[w.wfmt] if w.mx else m.MOE_BF16
+        shape = m.Shape(w.T, w.H, w.E, w.k, w.I, w.shared_I, dtype)
         self.layer = m.MoeLayer(shape, dev)
         self.layer.prepare(d(inp["w_gate"]), d(inp["w_up"]), d(inp["w_down"]),
                            d(inp["ws_gate"]), d(inp["ws_up"]), d(inp["ws_down"]))
@@ -379,7 +387,8 @@ class Bench:
                       for k in byts if k in stage_ms and stage_ms[k] > 0}
         dom = "gemm_gate_up_swiglu"
         achieved = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
-        kernel = "gemm_mx_kernel<2, 0>" if w.mx else "gemm_nt_kernel<2>"
+        fmt_code = {"e4m3": 0, "e2m3": 2, "e3m2": 3, "e2m1": 4}[w.wfmt]
+        kernel = f"gemm_mx_kernel<2, {fmt_code}>" if w.mx else "gemm_nt_kernel<2>"
         res = {
             "value": w.T * a.steps / elapsed,
             "ms_per_step": elapsed / a.steps * 1e3,
@@ -462,7 +471,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("mxfp8 (weight gradients too)" if a.mx_wgrad else "mxfp8") if w.mx else "bf16",
+        "dtype": _dtype_name(w, a.mx_wgrad),
         "data": "synthetic (seeded; random-init weights; supplied Zipf routing)"
                 if w.routing == "supplied" else "synthetic (seeded; random-init weights)",
         "config": {"workload": _describe(w),

@@ -8,7 +8,7 @@ libmoe's HIP kernels.
 from ._lib import (MOE_BF16, MOE_ERR_DEVICE_TIMEOUT, MOE_MXFP8, MOE_MXFP8_W4,  # noqa: F401
                    MOE_MXFP8_W6, MOE_MXFP8_W6E3M2, MOE_OK, MoeError,
                    MOE_SCHED_PERSISTENT, MOE_SCHED_PIPELINED, MOE_SCHED_STAGED,
-                   MoeSched, Shape, load,
+                   MoeSched, Shape, WEIGHT_FORMAT, load,
                    moe_combine, moe_decode_fwd, moe_dispatch, moe_expert_ffn, moe_layer_bwd, moe_layer_fwd,
                    moe_layout, moe_layout_noalloc, moe_packed_pointers, moe_packed_weight_bytes,
                    moe_prepare_weights,

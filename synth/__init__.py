@@ -83,6 +83,8 @@ def _named() -> dict:
                  router_std=1.0 / math.sqrt(2048)),
         Workload("kimi-bf16", zipf_s=1.0, **kimi),
         Workload("kimi-mx", zipf_s=1.2, mx=True, **kimi),
+        Workload("kimi-fp4", zipf_s=1.2, mx=True, wfmt="e2m1", **kimi),
+        Workload("kimi-fp6", zipf_s=1.2, mx=True, wfmt="e2m3", **kimi),
         Workload("dsv3-bf16", **dsv3),
         Workload("dsv3-mx", mx=True, **dsv3),
     ]
