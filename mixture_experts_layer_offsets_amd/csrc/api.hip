@@ -165,10 +165,9 @@ struct Work {
   float *dec_w, *dec_logits;
 };
 
-// Smallest minibatch the persistent forward accepts, and its count bound.
-long mk_min_minibatch(const Dims &d) {
-  return std::max(256L, (d.R + kMkMaxMinibatches - 1) / kMkMaxMinibatches);
-}
+// Smallest minibatch the persistent forward (and the pipelined schedule)
+// accepts, and its count bound.
+long mk_min_minibatch(const Dims &d) { return mk::min_minibatch(d.R); }
 
 size_t carve_work(const Dims &d, void *base, Work *w) {
   Carver c(base);
@@ -181,16 +180,16 @@ size_t carve_work(const Dims &d, void *base, Work *w) {
   t.dense_order = c.take<int32_t>(1);
   t.tile_start = c.take<int32_t>(d.E + 1);
   t.order = c.take<int32_t>(d.E);
-  t.max_nm = (int)((d.R + mk_min_minibatch(d) - 1) / mk_min_minibatch(d));
-  t.max_tiles = (int)((d.R + 255) / 256 + d.E + t.max_nm + 1);
-  t.mt_list = c.take<int32_t>(3L * t.max_tiles);
+  t.max_nm = mk::max_minibatches(d.R);
+  t.max_tiles = mk::max_row_tiles(d.R, d.E, t.max_nm);
+  t.mt_list = c.take<int32_t>(mk::mt_list_words(t.max_tiles));
   t.mt_off = c.take<int32_t>(t.max_nm + 1);
-  t.ph = c.take<int32_t>(3L * (2 * t.max_nm + 3));
-  t.cph = c.take<int32_t>(3L * (2 * t.max_nm + 1));
+  t.ph = c.take<int32_t>(mk::ph_words(t.max_nm));
+  t.cph = c.take<int32_t>(mk::cph_words(t.max_nm));
   t.tl = c.take<int32_t>(d.T);
   t.tl_off = c.take<int32_t>(t.max_nm + 1);
   t.tok_m = c.take<int32_t>(d.T);
-  t.n_counters = 2 + 3 * t.max_nm + t.max_tiles + (int)((d.T + 255) / 256) + 1;
+  t.n_counters = mk::counter_words(d.T, t.max_nm, t.max_tiles);
   t.counters = c.take<int32_t>(t.n_counters);
   t.pm_off = c.take<int32_t>((long)t.max_nm * (d.E + 1));
   t.pm_ts = c.take<int32_t>((long)t.max_nm * (d.E + 1));
@@ -554,19 +553,20 @@ int mk_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Save
   const int cus = device_cus();
   if (cus < 2) return MOE_ERR_HIP;
   MkArgs a{};
-  a.T = (int)d.T; a.H = (int)d.H; a.k = (int)d.k; a.E = (int)d.E; a.I = (int)d.I;
-  a.Is = (int)d.Is; a.R = (int)d.R; a.mx = d.mx;
+  mk::Plan &pl = a.plan;
+  pl.T = (int)d.T; pl.H = (int)d.H; pl.k = (int)d.k; pl.E = (int)d.E; pl.I = (int)d.I;
+  pl.Is = (int)d.Is; pl.R = (int)d.R; a.mx = d.mx;
   long mb = sc->minibatch_rows > 0 ? sc->minibatch_rows : 2048;
   mb = std::max(mb, mk_min_minibatch(d));
-  a.MB = (int)std::min(mb, d.R);
-  a.NM = (int)((d.R + a.MB - 1) / a.MB);
-  a.S = sc->ring_slots > 0 ? sc->ring_slots : 4;
-  a.n_comm = std::min(std::max(sc->comm_cus > 0 ? sc->comm_cus : 16, 1), cus - 1);
-  a.DCH = 16;
-  a.CT = 4;
+  pl.MB = (int)std::min(mb, d.R);
+  pl.NM = (int)((d.R + pl.MB - 1) / pl.MB);
+  pl.S = sc->ring_slots > 0 ? sc->ring_slots : 4;
+  pl.n_comm = std::min(std::max(sc->comm_cus > 0 ? sc->comm_cus : 16, 1), cus - 1);
+  pl.DCH = 16;
+  pl.CT = 4;
   // watchdog: microseconds -> 100 MHz ticks (default 2 s per wait)
-  a.watchdog_ticks = 100ULL * (sc->watchdog_us > 0 ? (unsigned long long)sc->watchdog_us : 2000000ULL);
-  a.x = x; a.perm = sv.perm; a.inv = sv.inv; a.offsets = sv.offsets; a.w = sv.w;
+  pl.watchdog_ticks = 100ULL * (sc->watchdog_us > 0 ? (unsigned long long)sc->watchdog_us : 2000000ULL);
+  a.x = x; a.perm = sv.perm; pl.inv = sv.inv; pl.offsets = sv.offsets; a.w = sv.w;
   a.x_perm = sv.x_perm; a.xq = sv.xq.q; a.xs = sv.xq.s;
   const long H = d.H, I = d.I, Is = d.Is;
   // routed gate/up and down, as the staged ffn_forward sets them up
@@ -601,20 +601,8 @@ int mk_forward(const Dims &d, const moe_sched *sc, const uint16_t *x, const Save
     }
   }
   a.y = sv.y; a.ys = sv.y_s; a.out = out;
-  a.mt_list = w.mt_list; a.mt_off = w.mt_off;
-  const int nph = 2 * w.max_nm + 3, ncph = 2 * w.max_nm + 1;
-  a.ph_kind = w.ph; a.ph_m = w.ph + nph; a.ph_off = w.ph + 2 * nph;
-  a.cph_kind = w.cph; a.cph_m = w.cph + ncph; a.cph_off = w.cph + 2 * ncph;
-  a.n_ph = 2 * a.NM + (d.shared ? 2 : 0);
-  a.n_cph = 2 * a.NM;
-  a.tl = w.tl; a.tl_off = w.tl_off; a.tok_m = w.tok_m;
-  int32_t *c = w.counters;
-  a.counters = c; a.n_counters = w.n_counters;
-  a.gemm_next = c; a.comm_next = c + 1;
-  a.disp_done = c + 2; a.g1m_done = a.disp_done + w.max_nm; a.g2m_done = a.g1m_done + w.max_nm;
-  a.g1_done = a.g2m_done + w.max_nm; a.sg1_done = a.g1_done + w.max_tiles;
-  a.sg2_done = a.sg1_done + (d.T + 255) / 256;
-  a.status = w.status;
+  mk::bind(pl, w.max_nm, w.max_tiles, w.mt_list, w.mt_off, w.ph, w.cph, w.tl, w.tl_off, w.tok_m,
+           w.counters, w.status);
   if (launch_layer_fwd_megakernel(a, cus, s)) return MOE_ERR_HIP;
   return MOE_OK;
 }
