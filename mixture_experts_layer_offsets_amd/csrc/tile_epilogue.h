@@ -5,13 +5,15 @@
 // global memory directly means one 1- or 2-byte store per value, 64 bytes per
 // half-wave at best; the SwiGLU backward also needs the saved g and u of
 // every value.  Both cost more than the tile's MFMAs at these shapes.  Here
-// the tile goes through LDS instead: the two 64 KB operand buffers, free once
-// the K loop is done, hold rows 0-127 (plane 0) and 128-255 (plane 1), each
-// row a whole number of 16-byte chunks with the chunk index XOR-ed by the row
-// (the accumulator layout's row pairs r, r + 4 then fall in different bank
-// groups).  All 256 threads then copy rows out, 16 bytes per lane, 32 or 64
-// lanes per row: full 128-byte lines.  The SwiGLU backward reads its g, u
-// span the same way, row-coalesced into LDS, and writes dg, du in place.
+// the tile goes through LDS instead, in the two 64 KB operand buffers, free
+// once the K loop is done.  bf16 results are staged as column runs (4 rows
+// of one column per 8-byte chunk, written with one LDS store per 4 values)
+// and read back as rows with gfx950's transposing LDS read; the fp32 staging
+// of the MX epilogue and the SwiGLU backward's g, u span use row-major
+// planes, each row a whole number of 16-byte chunks with the chunk index
+// XOR-ed by the row (the accumulator layout's row pairs r, r + 4 then fall
+// in different bank groups).  All 256 threads then copy rows out, 16 bytes
+// per lane: full 128-byte lines.
 #pragma once
 
 #include "gemm_common.h"
@@ -81,36 +83,109 @@ __device__ __forceinline__ int acc_row(int i, int v, int lane) {
   return 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// The wave's 128 x 128 accumulators as bf16 into its plane (512-byte rows).
-__device__ __forceinline__ void stage_acc_bf16(uint8_t *plane, const f32x16 (&acc)[4][4],
-                                               int wn0, int lane) {
-  const int ncol = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int v = 0; v < 16; v++)
-        *(uint16_t *)(plane + st_byte(acc_row(i, v, lane), 2 * (wn0 + 32 * j + ncol), 32)) =
-            (uint16_t)f32_to_bf16(acc[i][j][v]);
-}
-
 // Tile geometry handed to the epilogues.
 struct TileAt {
   int m0, n0, rowbase, Mg, wm0, wn0, lane, tid;
 };
 
-// Both planes' rows out to a row-major bf16 matrix C (pitch ldc elements),
-// columns from c0 (elements), `cols` valid columns of the tile.
-__device__ __forceinline__ void store_planes(uint8_t *L0, uint8_t *L1, int nch, const TileAt &t,
-                                             uint16_t *C, long ldc, long c0, int col_bytes) {
+// ---- Column-run staging of bf16 tiles
+//
+// Per 32 x 32 block, a lane's accumulators are runs of 4 consecutive rows of
+// one column.  Staged as bf16, a run is one 8-byte chunk: chunk (q, c) holds
+// rows 4q .. 4q+3 of column c at byte (q ncol + (c ^ ((c >> 2) & 4))) * 8 of a
+// plane of ncol columns, so a lane stages 4 values with one 8-byte LDS write
+// after two packed conversions.  The copy-out reads the runs back with
+// ds_read_b64_tr_b16, gfx950's transposing LDS read: within each 16-lane
+// group, output lane 4a + b receives element b of the 8-byte chunks
+// addressed by lanes a, 4 + a, 8 + a and 12 + a (measured on MI355X).  When
+// group lane 4s + a addresses column c + 8a + s of row quad q, output lane
+// 4a + b therefore receives row 4q + b, columns c + 8a .. c + 8a + 3, and a
+// second read four columns on gives the next four: a 16-byte row chunk per
+// lane, and for each row 16 lanes x 16 bytes of consecutive columns.  The XOR
+// of column bit 4 into bit 2 puts the 16 chunks of one group's read, and the
+// 16 chunks of one half-wave's write, in distinct banks.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 *lds_v4i16_t;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int run_off(int q, int c, int ncol) {
+  return (q * ncol + (c ^ ((c >> 2) & 4))) << 3;
+}
+
+// Two fp32 values as packed bf16, round to nearest even (v_cvt_pk_bf16_f32;
+// the same rounding as f32_to_bf16).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// The wave's 128 x 128 accumulators as bf16 runs into its plane (128 rows x
+// 256 columns: the wave's rows are plane rows 0-127, its columns wn0 + ...).
+__device__ __forceinline__ void stage_acc_runs(uint8_t *plane, const f32x16 (&acc)[4][4],
+                                               int wn0, int lane) {
+  const int qh = lane >> 5, c = wn0 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int vq = 0; vq < 4; vq++) {
+        const uint2 w = make_uint2(cvt_pk_bf16(acc[i][j][4 * vq], acc[i][j][4 * vq + 1]),
+                                   cvt_pk_bf16(acc[i][j][4 * vq + 2], acc[i][j][4 * vq + 3]));
+        *(uint2 *)(plane + run_off(8 * i + 2 * vq + qh, c + 32 * j, 256)) = w;
+      }
+}
+
+// Copies a run-staged plane (nq row quads x ncol columns, ncol a multiple of
+// 128) to a row-major bf16 matrix dst (pitch ld elements): rows below
+// rows_valid, columns below col_valid (a multiple of 8).  Units of (row quad,
+// 128 columns) go to the four waves in turn; each wave reads eight units
+// before it stores them.
+__device__ __forceinline__ void copy_runs_out(const uint8_t *plane, int ncol, int nq,
+                                              int rows_valid, int col_valid, uint16_t *dst,
+                                              long ld, int wave, int lane) {
+  constexpr int B = 8;
+  const int g = lane >> 4, y = lane & 15;
+  const int rc = 32 * g + 8 * (y & 3) + (y >> 2);  // column this lane addresses
+  const int oc = 32 * g + 8 * (y >> 2), orow = y & 3;  // what it receives
+  const int ncb = ncol >> 7, units = nq * ncb;
+  for (int u0 = wave; u0 < units; u0 += 4 * B) {
+    v4i16 lo[B], hi[B];
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+      const int u = min(u0 + 4 * k, units - 1);
+      const int q = u / ncb, cb = (u - q * ncb) << 7;
+      lo[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t)(plane + run_off(q, cb + rc, ncol)));
+      hi[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t)(plane + run_off(q, cb + rc + 4, ncol)));
+    }
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+      const int u = u0 + 4 * k;
+      const int q = u / ncb, cb = (u - q * ncb) << 7;
+      const int row = 4 * q + orow, col = cb + oc;
+      if (u < units && row < rows_valid && col < col_valid) {
+        const uint2 l = __builtin_bit_cast(uint2, lo[k]), h = __builtin_bit_cast(uint2, hi[k]);
+        *(uint4 *)(dst + (size_t)row * ld + col) = make_uint4(l.x, l.y, h.x, h.y);
+      }
+    }
+  }
+}
+
+// Both planes of a run-staged 256 x 256 tile out to C (pitch ldc), columns
+// from c0, `cols` valid columns.
+__device__ __forceinline__ void store_run_planes(const uint8_t *L0, const uint8_t *L1,
+                                                 const TileAt &t, uint16_t *C, long ldc, long c0,
+                                                 int cols) {
 #pragma unroll
   for (int pl = 0; pl < 2; pl++) {
     const int r0 = t.m0 + 128 * pl;
     const int rv = min(128, t.Mg - r0);
     if (rv > 0)
-      copy_rows_out(pl ? L1 : L0, nch, 128, rv, col_bytes,
-                    (uint8_t *)(C + (size_t)(t.rowbase + r0) * ldc + c0), ldc * 2, t.tid);
+      copy_runs_out(pl ? L1 : L0, 256, 32, rv, cols, C + (size_t)(t.rowbase + r0) * ldc + c0,
+                    ldc, t.tid >> 6, t.lane);
   }
 }
 
@@ -118,9 +193,9 @@ __device__ __forceinline__ void store_planes(uint8_t *L0, uint8_t *L1, int nch, 
 __device__ __forceinline__ void tile_epi_bf16(const GemmArgs &p, const f32x16 (&acc)[4][4],
                                               uint8_t *L0, uint8_t *L1, const TileAt &t) {
   __syncthreads();
-  stage_acc_bf16(t.wm0 ? L1 : L0, acc, t.wn0, t.lane);
+  stage_acc_runs(t.wm0 ? L1 : L0, acc, t.wn0, t.lane);
   __syncthreads();
-  store_planes(L0, L1, 32, t, (uint16_t *)p.C, p.ldc, t.n0, min(BN, p.N - t.n0) * 2);
+  store_run_planes(L0, L1, t, (uint16_t *)p.C, p.ldc, t.n0, min(BN, p.N - t.n0));
 }
 
 // EPI_SWIGLU: packed columns hold 64-column blocks [32 gate | 32 up].
@@ -137,32 +212,49 @@ __device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOpera
   uint8_t *plane = t.wm0 ? L1 : L0;
   __syncthreads();
   if (p.C2) {
-    stage_acc_bf16(plane, acc, t.wn0, t.lane);
+    stage_acc_runs(plane, acc, t.wn0, t.lane);
     __syncthreads();
-    store_planes(L0, L1, 32, t, (uint16_t *)p.C2, p.ldc2, t.n0, min(BN, p.N - t.n0) * 2);
+    store_run_planes(L0, L1, t, (uint16_t *)p.C2, p.ldc2, t.n0, min(BN, p.N - t.n0));
     __syncthreads();
   }
   const int ncol = t.lane & 31;
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int jj = 0; jj < 2; jj++) {
-      const int ca = t.wn0 / 2 + 32 * jj + ncol;  // tile-local a column
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int r = acc_row(i, v, t.lane);
-        const float av = silu_f(acc[i][2 * jj][v]) * acc[i][2 * jj + 1][v];
-        if constexpr (MX)
-          *(float *)(plane + st_byte(r, 4 * ca, 32)) = av;
-        else
-          *(uint16_t *)(plane + st_byte(r, 2 * ca, 16)) = (uint16_t)f32_to_bf16(av);
-      }
-    }
-  __syncthreads();
   const int a0 = t.n0 / 2, a_valid = min(BN / 2, I - a0);
   if constexpr (!MX) {
-    store_planes(L0, L1, 16, t, (uint16_t *)p.C, p.ldc, a0, a_valid * 2);
+    // a as bf16 runs: one plane (L0) of 256 rows x 128 columns
+    const int qh = t.lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int jj = 0; jj < 2; jj++) {
+        const int ca = t.wn0 / 2 + 32 * jj + ncol;  // tile-local a column
+#pragma unroll
+        for (int vq = 0; vq < 4; vq++) {
+          float av[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            av[e] = silu_f(acc[i][2 * jj][4 * vq + e]) * acc[i][2 * jj + 1][4 * vq + e];
+          const uint2 w = make_uint2(cvt_pk_bf16(av[0], av[1]), cvt_pk_bf16(av[2], av[3]));
+          *(uint2 *)(L0 + run_off((t.wm0 >> 2) + 8 * i + 2 * vq + qh, ca, 128)) = w;
+        }
+      }
+    __syncthreads();
+    copy_runs_out(L0, 128, 64, min(BM, t.Mg - t.m0), a_valid,
+                  (uint16_t *)p.C + (size_t)(t.rowbase + t.m0) * p.ldc + a0, p.ldc, t.tid >> 6,
+                  t.lane);
   } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int jj = 0; jj < 2; jj++) {
+        const int ca = t.wn0 / 2 + 32 * jj + ncol;  // tile-local a column
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int r = acc_row(i, v, t.lane);
+          const float av = silu_f(acc[i][2 * jj][v]) * acc[i][2 * jj + 1][v];
+          *(float *)(plane + st_byte(r, 4 * ca, 32)) = av;
+        }
+      }
+    __syncthreads();
     // 256 rows x 4 blocks of 32 values; 4 consecutive threads take one row
 #pragma unroll
     for (int it = 0; it < 4; it++) {
