@@ -209,9 +209,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
   const int nN = p.n_tiles_n;
   const int b = blockIdx.x;
   if (b >= MT * nN) return;
-  // consecutive blocks share the A row tile (n fastest); measured faster on
-  // this chip than XCD-grouped rasters for these shapes
-  const int mt = b / nN, nt = b - (b / nN) * nN;
+  int mt, nt;
+  tile_of_block(b, MT, nN, mt, nt);
   int lo = 0, hi = p.G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;

@@ -14,7 +14,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_mx_kernel(GemmArgs p, MxOperands m
   const int nN = p.n_tiles_n;
   const int b = blockIdx.x;
   if (b >= MT * nN) return;
-  const int mt = b / nN, nt = b - (b / nN) * nN;
+  int mt, nt;
+  tile_of_block(b, MT, nN, mt, nt);
   int lo = 0, hi = p.G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;

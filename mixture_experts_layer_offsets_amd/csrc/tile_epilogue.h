@@ -32,52 +32,6 @@ __device__ __forceinline__ int st_byte(int r, int b, int nch) {
   return st_off(r, b >> 4, nch) + (b & 15);
 }
 
-// Copy `rows` staged rows (nch chunks each) to dst (row pitch ld bytes):
-// rows < rows_valid, chunks whose first byte is < col_bytes.
-__device__ __forceinline__ void copy_rows_out(const uint8_t *plane, int nch, int rows,
-                                              int rows_valid, int col_bytes, uint8_t *dst,
-                                              long ld, int tid) {
-  const int n = rows * nch;
-  for (int idx = tid; idx < n; idx += NT) {
-    const int r = idx / nch, ch = idx - (idx / nch) * nch;
-    if (r < rows_valid && ch * 16 < col_bytes)
-      *(uint4 *)(dst + (size_t)r * ld + ch * 16) = *(const uint4 *)(plane + st_off(r, ch, nch));
-  }
-}
-
-// Copy rows from global memory (src, pitch ld bytes) into a plane; rows past
-// rows_valid or chunks past col_bytes are left unwritten (rows_valid >= 1,
-// col_bytes >= 16).  Each thread issues a batch of loads before its first LDS
-// store, so the copy costs a few memory round trips rather than one per
-// chunk; loads of skipped chunks read a valid chunk instead and are dropped.
-constexpr int kRowsInBatch = 16;
-
-__device__ __forceinline__ void copy_rows_in(uint8_t *plane, int nch, int rows, int rows_valid,
-                                             int col_bytes, const uint8_t *src, long ld,
-                                             int tid) {
-  const int n = rows * nch;
-  const int last_ch = (col_bytes - 1) >> 4;
-  for (int i0 = tid; i0 < n; i0 += NT * kRowsInBatch) {
-    uint4 v[kRowsInBatch];
-#pragma unroll
-    for (int u = 0; u < kRowsInBatch; u++) {
-      const int idx = min(i0 + NT * u, n - 1);
-      const int r = idx / nch, ch = idx - (idx / nch) * nch;
-      v[u] = *(const uint4 *)(src + (size_t)min(r, rows_valid - 1) * ld + min(ch, last_ch) * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < kRowsInBatch; u++)
-      asm volatile("" ::"v"(v[u].x), "v"(v[u].y), "v"(v[u].z), "v"(v[u].w));
-#pragma unroll
-    for (int u = 0; u < kRowsInBatch; u++) {
-      const int idx = i0 + NT * u;
-      const int r = idx / nch, ch = idx - (idx / nch) * nch;
-      if (idx < n && r < rows_valid && ch * 16 < col_bytes)
-        *(uint4 *)(plane + st_off(r, ch, nch)) = v[u];
-    }
-  }
-}
-
 // Row (within its 128-row plane) of accumulator element v of 32-row block i.
 __device__ __forceinline__ int acc_row(int i, int v, int lane) {
   return 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -291,62 +245,130 @@ __device__ __forceinline__ void tile_epi_swiglu(const GemmArgs &p, const MxOpera
 // way) to C:  dg = dA u silu'(g),  du = dA silu(g),
 // silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
 // The tile's 256 intermediate columns own a 512-column (1 KB) g|u span per
-// row; the 128 rows of one half of the tile fill both planes (rows 0-63 in
-// L0, 64-127 in L1), and the two waves that own those rows update them.
-template <int HALF>
-__device__ __forceinline__ void swiglu_bwd_half(const GemmArgs &p, const f32x16 (&acc)[4][4],
-                                                uint8_t *L0, uint8_t *L1, const TileAt &t) {
-  const int span_bytes = min(2 * BN, 2 * (p.N - t.n0)) * 2;  // valid bytes of the span
-  const long c0 = 2L * t.n0;                                // first packed column
-  const int r0 = t.m0 + 128 * HALF;
-  const int rv = min(128, t.Mg - r0);
-  __syncthreads();
-  if (rv > 0) {
-    const uint8_t *src = (const uint8_t *)(p.aux + (size_t)(t.rowbase + r0) * p.ldaux + c0);
-    copy_rows_in(L0, 64, 64, rv, span_bytes, src, p.ldaux * 2, t.tid);
-    if (rv > 64)
-      copy_rows_in(L1, 64, 64, rv - 64, span_bytes, src + (size_t)64 * p.ldaux * 2,
-                   p.ldaux * 2, t.tid);
-  }
-  __syncthreads();
-  if (rv > 0 && t.wm0 == 128 * HALF) {
-    const int ncol = t.lane & 31;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      uint8_t *pl = i < 2 ? L0 : L1;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int c = t.wn0 + 32 * j + ncol;        // tile-local intermediate column
-        const int pg = (c >> 5) * 64 + (c & 31);    // its gate column in the span
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          const int r = acc_row(i, v, t.lane) & 63;
-          uint16_t *G = (uint16_t *)(pl + st_byte(r, 2 * pg, 64));
-          uint16_t *U = (uint16_t *)(pl + st_byte(r, 2 * (pg + 32), 64));
-          const float gv = bf16_to_f32(*G), uv = bf16_to_f32(*U);
-          const float dA = acc[i][j][v];
-          const float s = sigmoid_f(gv);
-          *G = (uint16_t)f32_to_bf16(dA * uv * s * (1.0f + gv * (1.0f - s)));
-          *U = (uint16_t)f32_to_bf16(dA * gv * s);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if (rv > 0) {
-    uint8_t *dst = (uint8_t *)((uint16_t *)p.C + (size_t)(t.rowbase + r0) * p.ldc + c0);
-    copy_rows_out(L0, 64, 64, rv, span_bytes, dst, p.ldc * 2, t.tid);
-    if (rv > 64)
-      copy_rows_out(L1, 64, 64, rv - 64, span_bytes, dst + (size_t)64 * p.ldc * 2, p.ldc * 2,
-                    t.tid);
-  }
+// row.  The tile is done in eighths of 32 rows, software-pipelined over four
+// 32 KB LDS regions (P0, P1 in L0; Q0, Q1 in L1).  For eighth e:
+//  - its g|u rows arrive in Q[e & 1] by direct-to-LDS DMA, issued while
+//    eighth e - 1 is computed (row r in bytes [1024 r, 1024 r + 1024),
+//    16-byte chunk ch at slot ch ^ 2 (r & 3));
+//  - the two waves that own its rows write their fp32 dA as 4-row runs into
+//    P[e & 1] (16 bytes per run, run (q, c) at byte (256 q + c) * 16);
+//  - all four waves take runs in turn: a transposing read of Q gives a lane
+//    the 4-row runs of g and of u of its column (group lane 4s + a
+//    addresses row 4q + s at packed column pg(C) + 4a, so output lane
+//    4a + b holds column C + 4a + b), one 16-byte read its dA run; dg and
+//    du go back into P[e & 1] as bf16 runs once every dA run is read;
+//  - its rows are copied out with the transposing read while eighth e + 1
+//    is computed.
+// Every SIMD does a quarter of the sigmoid arithmetic.
+
+// Byte offset in a Q region of the 8-byte piece at packed column pc (a
+// multiple of 4) of row r.
+__device__ __forceinline__ int gu_off(int r, int pc) {
+  return (r << 10) + ((((pc >> 3) ^ ((r & 3) << 1))) << 4) + (((pc >> 2) & 1) << 3);
 }
+
+// Packed g column of intermediate column c: 64-column blocks [32 g | 32 u].
+__device__ __forceinline__ int packed_g(int c) { return ((c >> 5) << 6) + (c & 31); }
+
+constexpr int kBwdRegion = 32 * 1024;
 
 __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
                                                     const f32x16 (&acc)[4][4], uint8_t *L0,
                                                     uint8_t *L1, const TileAt &t) {
-  swiglu_bwd_half<0>(p, acc, L0, L1, t);
-  swiglu_bwd_half<1>(p, acc, L0, L1, t);
+  const int span_cols = min(2 * BN, 2 * (p.N - t.n0));  // valid packed columns
+  const int wave = t.tid >> 6, lane = t.lane;
+  const int g = lane >> 4, y = lane & 15;
+  const int rs4 = y >> 2, ra = y & 3;  // transposing read: row offset, column quad
+  const uint16_t *gu_base = p.aux + (size_t)(t.rowbase + t.m0) * p.ldaux + 2L * t.n0;
+  uint16_t *out_base = (uint16_t *)p.C + (size_t)(t.rowbase + t.m0) * p.ldc + 2L * t.n0;
+  auto rows_of = [&](int e) { return min(32, t.Mg - t.m0 - 32 * e); };
+  // g|u rows of eighth e into Q[e & 1] (rows past the tile read as zeros)
+  auto dma = [&](int e) {
+    const int rv = rows_of(e);
+    if (rv <= 0) return;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(gu_base + (size_t)32 * e * p.ldaux), (short)0, rv * (int)p.ldaux * 2,
+        kBufferDword3);
+    uint8_t *Q = L1 + (e & 1) * kBwdRegion;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int r = wave * 8 + k;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_ptr_t)(Q + (r << 10)), 16,
+          (uint32_t)(r * (int)p.ldaux * 2 + ((lane ^ ((r & 3) << 1)) << 4)), 0, 0, 0);
+    }
+  };
+  auto copy_out = [&](int e) {
+    const int rv = rows_of(e);
+    if (rv > 0)
+      copy_runs_out(L0 + (e & 1) * kBwdRegion, 512, 8, rv, span_cols,
+                    out_base + (size_t)32 * e * p.ldc, p.ldc, wave, lane);
+  };
+  __syncthreads();  // the operand buffers are free
+  dma(0);
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    uint8_t *P = L0 + (e & 1) * kBwdRegion;
+    const uint8_t *Q = L1 + (e & 1) * kBwdRegion;
+    const int rv = rows_of(e);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // eighth e's rows (and older stores)
+    __syncthreads();
+    if (e + 1 < 8) dma(e + 1);  // Q[(e + 1) & 1] was last read by eighth e - 1
+    if (rv > 0 && t.wm0 == 128 * (e >> 2)) {
+      const int i = e & 3, qh = lane >> 5;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int vq = 0; vq < 4; vq++) {
+          const int c = t.wn0 + 32 * j + (lane & 31);
+          *(float4 *)(P + (((2 * vq + qh) * 256 + c) << 4)) =
+              make_float4(acc[i][j][4 * vq], acc[i][j][4 * vq + 1], acc[i][j][4 * vq + 2],
+                          acc[i][j][4 * vq + 3]);
+        }
+    }
+    __syncthreads();
+    // runs: wave w takes units w, w + 4 (8 each): row quad u / 4, 64 columns
+    // (u % 4) * 64, group g their 16 columns from 16 g
+    uint2 og[8], ou[8];
+    if (rv > 0) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int u = wave + 4 * k, q = u >> 2;
+        const int C = ((u & 3) << 6) + 16 * g, c = C + y;
+        const int pr = packed_g(C) + 4 * ra;
+        const v4i16 gr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t)(Q + gu_off(4 * q + rs4, pr)));
+        const v4i16 ur = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t)(Q + gu_off(4 * q + rs4, pr + 32)));
+        const float4 da = *(const float4 *)(P + ((q * 256 + c) << 4));
+        const float dav[4] = {da.x, da.y, da.z, da.w};
+        float dg[4], du[4];
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+          const float gv = __uint_as_float((uint32_t)(uint16_t)gr[x] << 16);
+          const float uv = __uint_as_float((uint32_t)(uint16_t)ur[x] << 16);
+          const float sg = sigmoid_f(gv);
+          dg[x] = dav[x] * uv * sg * (1.0f + gv * (1.0f - sg));
+          du[x] = dav[x] * gv * sg;
+        }
+        og[k] = make_uint2(cvt_pk_bf16(dg[0], dg[1]), cvt_pk_bf16(dg[2], dg[3]));
+        ou[k] = make_uint2(cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3]));
+      }
+    }
+    if (e > 0) copy_out(e - 1);
+    __syncthreads();  // every dA run of eighth e has been read
+    if (rv > 0) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int u = wave + 4 * k, q = u >> 2;
+        const int c = ((u & 3) << 6) + 16 * g + y;
+        *(uint2 *)(P + run_off(q, packed_g(c), 512)) = og[k];
+        *(uint2 *)(P + run_off(q, packed_g(c) + 32, 512)) = ou[k];
+      }
+    }
+  }
+  __syncthreads();
+  copy_out(7);
 }
 
 }  // namespace moe
