@@ -19,7 +19,13 @@ HIP events around every kernel on the layer's stream; the permute stages'
 HBM fractions come from a second staged pass in which 1 GiB of scratch is
 written and then read back right before each of those stages (the 256 MB
 Infinity Cache then holds none of their inputs, and no dirty lines that the
-timed stage would have to write back).
+timed stage would have to write back).  The unflushed staged pass also reads
+the GEMM tiles' in-kernel counters (shader cycles against the 100 MHz real-
+time counter): "gemm_tiles" gives each GEMM stage's shader clock and the
+share of its cycles in the K loop and in the epilogue, and
+"mfma_frac_at_measured_clock" its MFMA fraction against the peak scaled to
+that clock (the published peaks assume 2.4 GHz; under these GEMMs the chip
+runs well below it).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule staged|pipelined] [--minibatch-rows N]
@@ -40,6 +46,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (the MX-scaled fp8 instruction)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_CLOCK_MHZ = 2400.0       # the engine clock the MFMA peaks are quoted at
 
 # GEMM stages whose operands are MXFP8 when the layer runs in MXFP8 (the
 # weight gradients stay bf16)
@@ -144,6 +151,24 @@ def sources_sha256(kernel: str) -> str:
     for f in KERNEL_SOURCES[kernel]:
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
+
+
+def _tile_clocks(st, names, steps) -> dict:
+    """Per GEMM stage, from the tiles' in-kernel counters (moe_sched
+    kernel_stamps: tiles, shader cycles, prologue + K-loop cycles, epilogue
+    cycles, 100 MHz real-time ticks): the shader clock the tiles ran at and
+    where their cycles went."""
+    out = {}
+    for i, name in enumerate(names):
+        tiles, cyc, loop, epi, ticks = (int(v) for v in st[i][:5])
+        if tiles == 0 or ticks == 0:
+            continue
+        out[name] = {"clock_mhz": cyc / ticks * 100.0,
+                     "tiles_per_step": tiles / steps,
+                     "cycles_per_tile": cyc / tiles,
+                     "loop_share": loop / cyc,
+                     "epilogue_share": epi / cyc}
+    return out
 
 
 def _dtype_name(w, mx_wgrad=False) -> str:
@@ -255,9 +280,11 @@ class Bench:
         self._keep = []          # ctypes objects that must outlive their calls
 
     # -- schedules
-    def sched(self, pipelined=False, mb=None, evs=None, hook=None):
+    def sched(self, pipelined=False, mb=None, evs=None, hook=None, stamps=None):
         import ctypes
         s = self.m.MoeSched()
+        if stamps is not None:
+            s.kernel_stamps = stamps.data_ptr()
         if pipelined:
             s.schedule = self.m.MOE_SCHED_PIPELINED
             s.minibatch_rows = self.a.minibatch_rows if mb is None else mb
@@ -327,12 +354,21 @@ class Bench:
         for _ in range(self.a.warmup):
             self.step()
         ev = [(self.events(self.n_f), self.events(self.n_b)) for _ in range(self.a.steps)]
-        scheds = [(self.sched(evs=f, hook=hooks[0]), self.sched(evs=b, hook=hooks[1]))
+        # the unflushed pass also collects the GEMM tiles' in-kernel timing
+        stamps = None if flush is not None else tuple(
+            torch.zeros((n, 8), dtype=torch.int64, device="cuda") for n in (self.n_f, self.n_b))
+        scheds = [(self.sched(evs=f, hook=hooks[0], stamps=stamps and stamps[0]),
+                   self.sched(evs=b, hook=hooks[1], stamps=stamps and stamps[1]))
                   for f, b in ev]
         torch.cuda.synchronize()
         for sf, sb in scheds:
             self.step(sf, sb)
         torch.cuda.synchronize()
+        if stamps is not None:
+            self.clocks = _tile_clocks(stamps[0].cpu().numpy(), FWD_STAGES, self.a.steps)
+            if self.w.backward:
+                self.clocks.update(_tile_clocks(stamps[1].cpu().numpy(), BWD_STAGES,
+                                                self.a.steps))
         ms = {}
         for i, name in enumerate(FWD_STAGES):
             ms[name] = float(np.mean([f[i].elapsed_time(f[i + 1]) for f, _ in ev]))
@@ -404,6 +440,12 @@ class Bench:
             "layer_bwd_ms": sum(stage_ms[n] for n in BWD_STAGES) if w.backward else None,
             "schedules_ms_per_step": {k: v / a.steps * 1e3 for k, v in wall.items()},
         }
+        clocks = getattr(self, "clocks", {})
+        if clocks:
+            res["gemm_tiles"] = clocks
+            res["mfma_frac_at_measured_clock"] = {
+                k: v * PEAK_CLOCK_MHZ / clocks[k]["clock_mhz"] for k, v in mfma.items()
+                if k in clocks and clocks[k]["clock_mhz"] > 0}
         if flushed is not None:
             res["permute_stage_ms_after_flush"] = {k: flushed[k] for k in byts if k in flushed}
             res["hbm_frac_without_flush"] = hbm_cached

@@ -172,6 +172,18 @@ typedef struct moe_sched {
                              its own on `stream` ahead of that stage (a
                              benchmark's cache flush); NULL = none */
   void *stage_hook_user;  /* passed to stage_hook */
+  uint64_t *kernel_stamps;
+                          /* optional device array of 8 * n_stage_events
+                             words, zeroed by the caller, staged schedule
+                             only: every tile of the expert GEMMs enqueued in
+                             stage i (the work after boundary i) adds, with
+                             device atomics, to words 8i + 0..4: tiles,
+                             shader cycles from tile start to epilogue end,
+                             of which the prologue and K loop, and the
+                             epilogue, and real-time ticks (100 MHz) -- so
+                             cycles / ticks * 100 MHz is the clock the tiles
+                             ran at.  Read it after the stream is done.
+                             NULL = no timing (the default) */
 } moe_sched;
 
 /* ------------------------------------------------------------------ sizes */

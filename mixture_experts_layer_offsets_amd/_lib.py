@@ -52,7 +52,8 @@ class MoeSched(ctypes.Structure):
                 ("comm_cus", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(c_void_p)), ("n_stage_events", ctypes.c_int32),
                 ("watchdog_us", ctypes.c_int32), ("mx_wgrad", ctypes.c_int32),
-                ("stage_hook", STAGE_HOOK), ("stage_hook_user", c_void_p)]
+                ("stage_hook", STAGE_HOOK), ("stage_hook_user", c_void_p),
+                ("kernel_stamps", c_void_p)]
 
 
 class MoeSavedView(ctypes.Structure):

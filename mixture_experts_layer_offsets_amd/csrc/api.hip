@@ -289,16 +289,43 @@ hipStream_t S(void *s) { return (hipStream_t)s; }
 
 // Stage boundary i: the caller's hook (if any), then its stage event i (if
 // any) recorded on the stream.
+// In-kernel timing (moe_sched.kernel_stamps, staged schedule): the counter
+// block of the stage being enqueued, per host thread; stage i is the work
+// after boundary i.
+thread_local unsigned long long *tl_stamps = nullptr;
+thread_local int tl_stage = 0, tl_nstages = 0;
+
+struct StampScope {
+  StampScope(const moe_sched *sc, bool staged) {
+    const bool on = sc && staged && sc->kernel_stamps && sc->n_stage_events > 0;
+    tl_stamps = on ? (unsigned long long *)sc->kernel_stamps : nullptr;
+    tl_stage = 0;
+    tl_nstages = on ? sc->n_stage_events : 0;
+  }
+  ~StampScope() { tl_stamps = nullptr; }
+};
+
 struct Stages {
   const moe_sched *sc;
   hipStream_t s;
   void mark(int i) const {
+    tl_stage = i;
     if (!sc || i >= sc->n_stage_events) return;
     if (sc->stage_hook) sc->stage_hook(sc->stage_hook_user, i);
     if (sc->stage_events && sc->stage_events[i])
       hipEventRecord((hipEvent_t)sc->stage_events[i], s);
   }
 };
+
+}  // namespace
+
+unsigned long long *moe::current_stamps() {
+  return tl_stamps && tl_stage < tl_nstages ? tl_stamps + (size_t)kStampWords * tl_stage
+                                            : nullptr;
+}
+
+namespace {
+
 
 // Pack one expert set: gate/up interleaved in 32-wide blocks (g block, then
 // u block, per 64) so one GEMM tile holds matching g and u columns; every
@@ -1186,6 +1213,7 @@ int moe_layer_fwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   carve_packed(d, packed, &p);
   hipStream_t s = S(stream);
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k;
+  const StampScope stamp_scope(sched, mode == MOE_SCHED_STAGED);
   const Stages st{sched, s};
   st.mark(0);
   launch_fill_i32(w.status, 1, MOE_OK, s);
@@ -1281,6 +1309,7 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   carve_packed(d, packed, &p);
   hipStream_t s = S(stream);
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, k = (int)d.k;
+  const StampScope stamp_scope(sched, mode == MOE_SCHED_STAGED);
   const Stages st{sched, s};
   st.mark(0);
   launch_fill_i32(w.status, 1, MOE_OK, s);

@@ -258,6 +258,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
   const int m0 = mt * BM, n0 = (rem - mt * p.n_tiles_n) * BN;
   const int koff = p.offsets[g];
   const int Kg = p.offsets[g + 1] - koff;
+  TileClock clk;
+  clk.start(p);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -375,7 +377,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
     if (kt < nk) stage(L0, L1, kt);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
   }
+  clk.loop_done(p);
   epilogue<true, EPI>(p, acc, g, m0, n0, 0, p.M, wm0, wn0, lane);
+  clk.finish(p);
 }
 
 template <bool WGRAD, bool B_KC>
@@ -392,6 +396,7 @@ static void launch_epi(const GemmArgs &p, int epi, int grid, hipStream_t s) {
 
 void launch_gemm_rows(const GemmArgs &p0, int epi, bool b_kcontig, int max_rows, hipStream_t s) {
   GemmArgs p = p0;
+  p.stamps = current_stamps();
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long m_tiles = (long)max_rows / BM + p.G;
   const long grid = m_tiles * p.n_tiles_n;
@@ -412,6 +417,7 @@ void launch_gemm_rows(const GemmArgs &p0, int epi, bool b_kcontig, int max_rows,
 
 void launch_gemm_wgrad(const GemmArgs &p0, int epi, hipStream_t s) {
   GemmArgs p = p0;
+  p.stamps = current_stamps();
   p.n_tiles_m = (p.M + BM - 1) / BM;
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long grid = (long)p.G * p.n_tiles_m * p.n_tiles_n;

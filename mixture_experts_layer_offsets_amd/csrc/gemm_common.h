@@ -32,14 +32,71 @@ __device__ __forceinline__ void transpose8x8(const uint4 *in, uint4 *out) {
   }
 }
 
+// 4 x 4 transpose of fp32 values across the four lanes of a quad: lane s of
+// the quad holds x[0..3], rows 0..3 of its column s; afterwards it holds row
+// s of columns 0..3.  Two butterfly stages of DPP quad permutations (swap
+// with lane ^ 1, then with lane ^ 2), each lane sending the value its
+// partner keeps.
+__device__ __forceinline__ void quad_transpose4(float (&x)[4], int s) {
+  const bool odd = s & 1, hi = s & 2;
+  auto swap1 = [](float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  };
+  auto swap2 = [](float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  };
+  const float r0 = swap1(odd ? x[0] : x[1]), r1 = swap1(odd ? x[2] : x[3]);
+  const float y0 = odd ? r0 : x[0], y1 = odd ? x[1] : r0;
+  const float y2 = odd ? r1 : x[2], y3 = odd ? x[3] : r1;
+  const float t0 = swap2(hi ? y0 : y2), t1 = swap2(hi ? y1 : y3);
+  x[0] = hi ? t0 : y0;
+  x[1] = hi ? t1 : y1;
+  x[2] = hi ? y2 : t0;
+  x[3] = hi ? y3 : t1;
+}
+
 // Epilogue shared by both kernels.  acc[i][j][v] holds row
 // wm0 + 32i + 8(v/4) + 4(lane/32) + v%4 and column wn0 + 32j + lane%32 of the tile.
+// Weight-gradient fp32 outputs: each 4-row run of the four columns a lane
+// quad holds is transposed across the quad (quad_transpose4), so a lane
+// writes 4 consecutive columns of one row with one 16-byte store, and a
+// wave's store covers eight whole 128-byte lines.
 template <bool WGRAD, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &p, f32x16 (&acc)[4][4], int g, int m0,
                                          int n0, int rowbase, int Mg, int wm0, int wn0,
                                          int lane) {
   const int N = p.N;
   const int ncol = lane & 31;
+  if constexpr (WGRAD && (EPI == EPI_F32 || EPI == EPI_WGRAD_GU)) {
+    const int s = lane & 3, c4 = ncol & ~3;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int vq = 0; vq < 4; vq++) {
+          float x[4] = {acc[i][j][4 * vq], acc[i][j][4 * vq + 1], acc[i][j][4 * vq + 2],
+                        acc[i][j][4 * vq + 3]};
+          quad_transpose4(x, s);
+          const int m = m0 + wm0 + 32 * i + 8 * vq + 4 * (lane >> 5) + s;
+          const int n = n0 + wn0 + 32 * j + c4;
+          if (m < Mg && n < N) {
+            if constexpr (EPI == EPI_F32) {
+              float4 v = make_float4(x[0], x[1], x[2], x[3]);
+              if (p.bias) {
+                v.x += p.bias[n]; v.y += p.bias[n + 1]; v.z += p.bias[n + 2]; v.w += p.bias[n + 3];
+              }
+              *(float4 *)((float *)p.C + (size_t)g * p.sC + (size_t)m * p.ldc + n) = v;
+            } else {
+              // packed columns -> dW_gate / dW_up [g][h][i]
+              const int ii = (n >> 6) * 32 + (n & 31);
+              float *D = (float *)(((n >> 5) & 1) ? p.C2 : p.C) + (size_t)g * p.sC;
+              *(float4 *)(D + (size_t)m * p.ldc + ii) = make_float4(x[0], x[1], x[2], x[3]);
+            }
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
 #pragma unroll
@@ -126,6 +183,32 @@ __device__ __forceinline__ void tile_of_block(int b, int MT, int nN, int &mt, in
   mt = kk / w;
   nt = (beta << 3) + kk - (kk / w) * w;
 }
+
+// In-kernel timing of one tile (kernels.h, kStamp*): read only when the
+// launch carries a counter block, added by thread 0 with vector atomics.
+struct TileClock {
+  unsigned long long c0 = 0, r0 = 0, c1 = 0;
+  __device__ __forceinline__ void start(const GemmArgs &p) {
+    if (p.stamps) {
+      c0 = __builtin_amdgcn_s_memtime();
+      r0 = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  __device__ __forceinline__ void loop_done(const GemmArgs &p) {
+    if (p.stamps) c1 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void finish(const GemmArgs &p) {
+    if (p.stamps && threadIdx.x == 0) {
+      const unsigned long long c2 = __builtin_amdgcn_s_memtime();
+      const unsigned long long r2 = __builtin_amdgcn_s_memrealtime();
+      atomicAdd(p.stamps + kStampTiles, 1ull);
+      atomicAdd(p.stamps + kStampCycles, c2 - c0);
+      atomicAdd(p.stamps + kStampLoop, c1 - c0);
+      atomicAdd(p.stamps + kStampEpilogue, c2 - c1);
+      atomicAdd(p.stamps + kStampTicks, r2 - r0);
+    }
+  }
+};
 
 constexpr uint32_t kBufferDword3 = 0x00020000;  // raw buffer, gfx9 family
 

@@ -47,6 +47,7 @@ static void launch_mx_fmt(const GemmArgs &p, const MxOperands &mx, int epi, cons
 void launch_gemm_rows_mx(const GemmArgs &p0, const MxOperands &mx, int epi, int max_rows,
                          hipStream_t s) {
   GemmArgs p = p0;
+  p.stamps = current_stamps();
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long grid = ((long)max_rows / BM + p.G) * p.n_tiles_n;
   if (grid <= 0) return;
@@ -245,6 +246,7 @@ void launch_quant_cols_mx(const uint16_t *src, int R, int C, const int32_t *offs
 
 void launch_gemm_mx_wgrad(const GemmArgs &p0, const MxOperands &mx, int epi, hipStream_t s) {
   GemmArgs p = p0;
+  p.stamps = current_stamps();
   p.n_tiles_m = (p.M + BM - 1) / BM;
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long grid = (long)p.G * p.n_tiles_m * p.n_tiles_n;

@@ -117,7 +117,26 @@ struct GemmArgs {
   const int32_t *order;       // [G] group processing order (weight-gradient mode)
   int G, M, N, K;
   int n_tiles_m, n_tiles_n;
+  unsigned long long *stamps;  // optional per-tile timing counters (TileClock)
 };
+
+// Counter block of the in-kernel timing of a stage's GEMM tiles (device,
+// 8 words, zeroed by the caller): every tile adds, from thread 0 of its
+// workgroup, the words below.  Shader cycles from s_memtime, real time from
+// the 100 MHz s_memrealtime, so cycles / ticks * 100 MHz is the clock the
+// tiles ran at.
+enum {
+  kStampTiles = 0,      // tiles
+  kStampCycles = 1,     // shader cycles, tile start to epilogue end
+  kStampLoop = 2,       // of which prologue + K loop
+  kStampEpilogue = 3,   // of which epilogue
+  kStampTicks = 4,      // real-time ticks (100 MHz), tile start to end
+  kStampWords = 8
+};
+
+// The counter block the GEMMs launched now add to (nullptr = none): set by
+// the layer call for the stage it is enqueueing (host, per thread).
+unsigned long long *current_stamps();
 
 // Row-ragged grouped GEMM: for group g, rows [offsets[g], offsets[g+1]) of A
 // (K-contiguous, [rows][K]) times B_g (K-contiguous [N][K], or N-contiguous

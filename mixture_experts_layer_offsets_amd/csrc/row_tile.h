@@ -27,6 +27,8 @@ namespace moe {
 template <int EPI>
 __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0, int rowbase,
                                         int Mg, uint16_t *L0, uint16_t *L1) {
+  TileClock clk;
+  clk.start(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
@@ -147,6 +149,7 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
   if (kt < nk) stage(L0, L1, kt);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
   __syncthreads();                      // the epilogue reuses both buffers
+  clk.loop_done(p);
   const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
   if constexpr (EPI == EPI_BF16)
     tile_epi_bf16(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
@@ -154,6 +157,7 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
     tile_epi_swiglu<false>(p, nullptr, acc, (uint8_t *)L0, (uint8_t *)L1, t);
   else
     tile_epi_swiglu_bwd(p, acc, (uint8_t *)L0, (uint8_t *)L1, t);
+  clk.finish(p);
 }
 
 // Grouped GEMMs on MXFP8 operands (E4M3 codes with one E8M0 scale per 32
@@ -193,6 +197,8 @@ __device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 2)) & 3; }
 template <int EPI, int BFMT = kMxE4M3>
 __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx, int g, int m0,
                                         int n0, int rowbase, int Mg, uint8_t *L0, uint8_t *L1) {
+  TileClock clk;
+  clk.start(p);
   // B bytes per row and stage, and B DMA instructions per wave and stage
   constexpr int BKB = BFMT == kMxE2M1 ? MXK / 2 : MXK;
   constexpr int NBQ = BFMT == kMxE2M1 ? 4 : 8;
@@ -358,6 +364,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   if (kt < nk) stage(L0, L1, kt, sa0, sb0);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
   __syncthreads();  // the epilogue reuses both buffers
+  clk.loop_done(p);
 
   const TileAt t{m0, n0, rowbase, Mg, wm0, wn0, lane, tid};
   if constexpr (EPI == EPI_BF16) {
@@ -373,6 +380,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   } else {
     tile_epi_swiglu_bwd(p, acc, L0, L1, t);
   }
+  clk.finish(p);
 }
 
 }  // namespace moe
