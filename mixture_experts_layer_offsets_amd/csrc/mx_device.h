@@ -6,44 +6,45 @@
 
 namespace moe {
 
-__device__ __forceinline__ uint32_t e4m3_encode(float v, bool neg) {
-  const float a = fabsf(v);
-  const uint32_t sign = neg ? 0x80u : 0u;
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // spacing 2^-9
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // round to 3 mantissa bits
-  const int e = (int)(r >> 23) - 127;
-  return sign | ((uint32_t)(e + 7) << 3) | ((r >> 20) & 7u);
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t ex = (c >> 3) & 15u, m = c & 7u;
-  const float mag = ex ? ldexpf((float)(8u + m), (int)ex - 10) : ldexpf((float)m, -9);
-  return (c & 0x80u) ? -mag : mag;
-}
-
-// E4M3 code of a value with |v| <= 448 (sign bit from `neg`), and in `mag`
-// the magnitude that code stands for (the rounded |v|).
-__device__ __forceinline__ uint32_t e4m3_encode_mag(float v, bool neg, float *mag) {
-  const float a = fabsf(v);
-  const uint32_t sign = neg ? 0x80u : 0u;
-  if (a < 0.015625f) {  // subnormal codes: spacing 2^-9
-    const float q = rintf(a * 512.0f);
-    *mag = q * 0.001953125f;
-    return sign | (uint32_t)q;
-  }
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
-  *mag = __uint_as_float(r);
-  const int e = (int)(r >> 23) - 127;
-  return sign | ((uint32_t)(e + 7) << 3) | ((r >> 20) & 7u);
-}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int floor_log2(float a) {  // a > 0
   const uint32_t u = __float_as_uint(a);
   const int ex = (int)(u >> 23);
   if (ex) return ex - 127;
   return -149 + (31 - __clz(u & 0x7FFFFFu));
+}
+
+// E8M0 exponent of a block from its largest magnitude: the element format's
+// largest power of two (2^8 for E4M3) is lined up with amax's, clamped to the
+// scale's range; an all-zero block takes the smallest scale.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int s = floor_log2(amax) - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// Four values to four E4M3 codes (one little-endian dword) at scale 2^s:
+// each is scaled by 2^-s, clamped to +-448 and rounded to nearest even by the
+// packed fp8 conversion.  The sign of a code is that of the value: adding
+// +0.0 first turns -0.0 into +0.0, while a negative value whose scaled form
+// underflows keeps its sign (-0.0, code 0x80).  With deq, the values the
+// codes stand for (times 2^s) are written there.
+__device__ __forceinline__ uint32_t e4m3_pack4(const float *x, int s, float *deq) {
+  float sc[4];
+#pragma unroll
+  for (int b = 0; b < 4; b++) sc[b] = fminf(fmaxf(ldexpf(x[b] + 0.0f, -s), -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sc[0], sc[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sc[2], sc[3], w, true);
+  if (deq) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    deq[0] = ldexpf(lo.x, s);
+    deq[1] = ldexpf(lo.y, s);
+    deq[2] = ldexpf(hi.x, s);
+    deq[3] = ldexpf(hi.y, s);
+  }
+  return (uint32_t)w;
 }
 
 // MXFP8 conversion of one block of 32 values (E4M3 elements, E8M0 scale):
@@ -56,25 +57,9 @@ __device__ __forceinline__ uint32_t mx_block32(const float *v, uint32_t *w, floa
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-  int s = -127;
-  if (amax > 0.0f) {
-    s = floor_log2(amax) - 8;
-    s = s < -127 ? -127 : (s > 127 ? 127 : s);
-  }
+  const int s = mx_scale_exp(amax);
 #pragma unroll
-  for (int q = 0; q < 8; q++) {
-    uint32_t d = 0;
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const float x = v[q * 4 + b];
-      const float sc = fminf(fmaxf(ldexpf(x, -s), -448.0f), 448.0f);
-      float mag;
-      const uint32_t c = e4m3_encode_mag(sc, x < 0.0f, &mag);
-      d |= c << (8 * b);
-      if (deq) deq[q * 4 + b] = ldexpf(x < 0.0f ? -mag : mag, s);
-    }
-    w[q] = d;
-  }
+  for (int q = 0; q < 8; q++) w[q] = e4m3_pack4(v + 4 * q, s, deq ? deq + 4 * q : nullptr);
   return (uint32_t)(s + 127);
 }
 
@@ -95,28 +80,10 @@ __device__ __forceinline__ uint32_t mx_quad8(const float *v, uint2 *codes, float
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
-  amax = quad_max(amax);
-  int s = -127;
-  if (amax > 0.0f) {
-    s = floor_log2(amax) - 8;
-    s = s < -127 ? -127 : (s > 127 ? 127 : s);
-  }
-  uint32_t w[2];
-#pragma unroll
-  for (int q = 0; q < 2; q++) {
-    uint32_t d = 0;
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const float x = v[q * 4 + b];
-      const float sc = fminf(fmaxf(ldexpf(x, -s), -448.0f), 448.0f);
-      float mag;
-      const uint32_t c = e4m3_encode_mag(sc, x < 0.0f, &mag);
-      d |= c << (8 * b);
-      deq[q * 4 + b] = ldexpf(x < 0.0f ? -mag : mag, s);
-    }
-    w[q] = d;
-  }
-  *codes = make_uint2(w[0], w[1]);
+  const int s = mx_scale_exp(quad_max(amax));
+  const uint32_t w0 = e4m3_pack4(v, s, deq);
+  const uint32_t w1 = e4m3_pack4(v + 4, s, deq ? deq + 4 : nullptr);
+  *codes = make_uint2(w0, w1);
   return (uint32_t)(s + 127);
 }
 
