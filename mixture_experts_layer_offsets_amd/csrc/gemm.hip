@@ -345,10 +345,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt) {
+    // `first`: stage 0, whose successor the prologue issued in full
+    auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt, auto first) {
       load(Lc, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+      if constexpr (decltype(first)::value)
+        mma(0);
+      else
+        mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 1; ks < 3; ks++) {
         load(Lc, ks + 1, (ks + 1) & 1);
@@ -362,19 +367,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       mma_dma(1, Lc, kt + 2, 0);  // first half of Lc's refill
     };
+    // Prologue: stages 0 and 1 in flight together, then the wait for stage 0
+    // alone (its 16 DMAs were issued first), so a short contraction (a few
+    // stages: experts with few rows) pays one memory latency up front, not
+    // two.
 #pragma unroll
     for (int q = 0; q < 16; q++) dma(L0, 0, q);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 8; q++) dma(L1, 1, q);
+    for (int q = 0; q < 16; q++) dma(L1, 1, q);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));
+    barrier_after_wait();
     load(L0, 0, 0);
-    int kt = 0;
+    stage(L0, L1, 0, std::true_type{});
+    int kt = 1;
     for (; kt + 2 <= nk; kt += 2) {
-      stage(L0, L1, kt);
-      stage(L1, L0, kt + 1);
+      stage(L1, L0, kt, std::false_type{});
+      stage(L0, L1, kt + 1, std::false_type{});
     }
-    if (kt < nk) stage(L0, L1, kt);
+    if (kt < nk) stage(L1, L0, kt, std::false_type{});
     __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
   }
   clk.loop_done(p);

@@ -118,10 +118,15 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt) {
+  // `first`: stage 0, whose successor the prologue issued in full
+  auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt, auto first) {
     load(Lc, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+    if constexpr (decltype(first)::value)
+      mma(0);
+    else
+      mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 1; ks < 3; ks++) {
       load(Lc, ks + 1, (ks + 1) & 1);
@@ -135,18 +140,20 @@ __device__ __forceinline__ void nt_tile(const GemmArgs &p, int g, int m0, int n0
     __builtin_amdgcn_sched_barrier(0);
     mma_dma(1, Lc, kt + 2, 0);  // first half of Lc's refill
   };
+  // Prologue: stages 0 and 1 in flight together, then the wait for stage 0
+  // alone (its 16 DMAs were issued first): one memory latency per tile.
   issue(L0, 0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 8; q++) dma(L1, 1, q);
+  issue(L1, 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));
+  barrier_after_wait();
   load(L0, 0, 0);
-  int kt = 0;
+  stage(L0, L1, 0, std::true_type{});
+  int kt = 1;
   for (; kt + 2 <= nk; kt += 2) {
-    stage(L0, L1, kt);
-    stage(L1, L0, kt + 1);
+    stage(L1, L0, kt, std::false_type{});
+    stage(L0, L1, kt + 1, std::false_type{});
   }
-  if (kt < nk) stage(L0, L1, kt);
+  if (kt < nk) stage(L1, L0, kt, std::false_type{});
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the zero fills
   __syncthreads();                      // the epilogue reuses both buffers
   clk.loop_done(p);
@@ -349,12 +356,15 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
     }
     load_scales(min(kt + 2, nk - 1), sa, sb);
   };
+  // Prologue: stages 0 and 1 (and their scales) in flight together, then
+  // the wait for stage 0 and its scales alone (stage 1's 8 + NBQ DMAs and 8
+  // scale loads were issued after them): one memory latency per tile.
   issue(L0, 0);
   load_scales(0, sa0, sb0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
   issue(L1, 1);
   load_scales(min(1, nk - 1), sa1, sb1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(8 + NBQ + 8));
+  barrier_after_wait();
   load(L0, 0, 0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
