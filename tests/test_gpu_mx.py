@@ -36,7 +36,10 @@ def _edge_rows(T, H, seed):
     """bf16 rows whose 32-blocks cover the conversion's edge cases: zero
     blocks, signed zeros, a lone nonzero, values that round to zero,
     saturation at 448, round-half ties, very large and very small (bf16
-    subnormal) magnitudes, and plain normal data at scales 2^-30 .. 2^30."""
+    subnormal) magnitudes, tiny values beside a huge block maximum (scaled by
+    2^-s they underflow fp32: the sign rule must still give negative values
+    the sign bit), -0.0 inside nonzero blocks, and plain normal data at
+    scales 2^-30 .. 2^30."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, H))
     nb = H // 32
@@ -64,6 +67,12 @@ def _edge_rows(T, H, seed):
             v[:] = rng.standard_normal(32) * 2.0 ** 100
         elif kind == 6:          # bf16 subnormals
             v[:] = rng.standard_normal(32) * 2.0 ** -130
+        elif kind == 7:          # huge maximum, the rest underflow once scaled
+            v[:] = rng.standard_normal(32) * 2.0 ** rng.choice([-60, -100, -130], 32)
+            v[rng.integers(32)] = rng.choice([-1.0, 1.0]) * 2.0 ** 100
+        elif kind == 8:          # -0.0 (and +0.0) among normal values
+            v[rng.integers(0, 32, 8)] = -0.0
+            v[rng.integers(0, 32, 4)] = 0.0
     assert np.all(np.isfinite(x.astype(np.float32)))
     return synth.f32_to_bf16_bits(x.astype(np.float32))
 
