@@ -85,7 +85,11 @@ enum {
  * hidden size, top-k and expert count [KC §03], expert intermediate size
  * [KC §02], plus the token count and the datatype.
  * Limits: 1 <= T; 1 <= k <= 16; 1 <= E <= 1024; H, I and shared_inter
- * multiples of 64 (of 128 for the MX types); R = T*k < 2^31; H*E < 2^31. */
+ * multiples of 64 (of 128 for the MX types); R = T*k < 2^31; H*E < 2^31.
+ * The MX types also: with Rp = R + 127 E rounded up to a multiple of 128
+ * (the routed rows padded per expert), Rp < 2^23, Rp * max(H, 2 I,
+ * 2 shared_inter) < 2^36 and E * H * max(I, shared_inter) < 2^35 (32-bit
+ * byte counts of the scaled operands).  Other shapes: MOE_ERR_UNSUPPORTED. */
 typedef struct moe_shape {
   int32_t tokens;       /* T */
   int32_t hidden;       /* H */

@@ -67,6 +67,17 @@ int check_shape(const moe_shape *s, Dims *d) {
   if (s->hidden % mult || s->inter % mult || s->shared_inter % mult) return MOE_ERR_UNSUPPORTED;
   if (s->experts > 1024 || s->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)s->hidden * s->experts >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype != MOE_BF16) {
+    // 32-bit byte counts of the MX GEMMs' buffer descriptors: the per-32
+    // scales of the routed rows (padded per expert to 128, the weight
+    // gradients' contraction) and of every expert's weights, and 256 rows of
+    // the weight gradients' transposed codes
+    const long wide = std::max((long)s->hidden, 2L * std::max(s->inter, s->shared_inter));
+    const long Rp = (R + 127L * s->experts + 127) / 128 * 128;
+    if (Rp >= (1L << 23) || Rp * wide >= (1L << 36) ||
+        (long)s->experts * s->hidden * std::max(s->inter, s->shared_inter) >= (1L << 35))
+      return MOE_ERR_UNSUPPORTED;
+  }
   d->T = s->tokens; d->H = s->hidden; d->E = s->experts; d->k = s->top_k; d->I = s->inter;
   d->Is = s->shared_inter; d->R = R; d->mx = s->dtype != MOE_BF16;
   d->shared = s->shared_inter > 0;

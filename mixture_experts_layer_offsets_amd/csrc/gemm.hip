@@ -268,10 +268,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
     for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
 
   if (Kg > 0) {
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.A + (size_t)koff * p.lda + m0), (short)0, Kg * (int)p.lda * 2, kBufferDword3);
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.B + (size_t)koff * p.ldb + n0), (short)0, Kg * (int)p.ldb * 2, kBufferDword3);
+    const uint16_t *gA = p.A + (size_t)koff * p.lda + m0;  // the group's first row,
+    const uint16_t *gB = p.B + (size_t)koff * p.ldb + n0;  // from the tile's column
     // DMA: instruction i of wave w fills LDS rows 2 (8w + i) + {0, 1}; lane L
     // writes chunk L % 32 of row 2 (8w + i) + L / 32 and so fetches the global
     // chunk that the swizzle maps there.
@@ -284,20 +282,29 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
       ob[i] = (uint32_t)(row * (int)p.ldb * 2 + c * 16);
     }
     const int nk = (Kg + 63) / 64;
-    // DMA instruction q (0-7: A rows, 8-15: B rows) of stage kt into L; a
-    // stage past the end selects an empty descriptor (zero fill, no traffic)
-    const __amdgpu_buffer_rsrc_t rNone =
-        __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, 0, kBufferDword3);
-    auto dma = [&](uint16_t *L, int kt, int q) {
-      const bool live = kt < nk;
+    // The descriptor of stage kt's A (B) rows starts at the stage's first
+    // row, so its byte count and offsets stay within 64 rows however long
+    // the group; it ends at column M (N) of the group's last row, so rows
+    // past the group and a partial column tile read zeros, nothing outside
+    // the operands; a stage past the end gets zero bytes (zero fill, no
+    // traffic).  Built once per stage and operand: built per instruction, or
+    // selected between descriptors, it cost branches and private memory.
+    auto desc = [&](int kt, bool a) {
+      const int rows = Kg - kt * 64;
+      const int ld = a ? (int)p.lda : (int)p.ldb;
+      const int bytes =
+          rows <= 0 ? 0 : ((min(rows, 64) - 1) * ld + (a ? p.M - m0 : p.N - n0)) * 2;
+      return __builtin_amdgcn_make_buffer_rsrc((void *)((a ? gA : gB) + (size_t)kt * 64 * ld),
+                                               (short)0, bytes, kBufferDword3);
+    };
+    // DMA instruction q (0-7: A rows, 8-15: B rows) of a stage into L
+    auto dma = [&](__amdgpu_buffer_rsrc_t r, uint16_t *L, int q) {
       if (q < 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rA : rNone,
-                                                 (lds_ptr_t)(L + (wave * 8 + q) * 512), 16, oa[q],
-                                                 live ? kt * 64 * (int)p.lda * 2 : 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(L + (wave * 8 + q) * 512), 16,
+                                                 oa[q], 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            live ? rB : rNone, (lds_ptr_t)(L + 64 * BM + (wave * 8 + q - 8) * 512), 16,
-            ob[q - 8], live ? kt * 64 * (int)p.ldb * 2 : 0, 0, 0);
+            r, (lds_ptr_t)(L + 64 * BM + (wave * 8 + q - 8) * 512), 16, ob[q - 8], 0, 0, 0);
     };
     // fragment addresses: lane l in 16-lane group q = l / 16, j = l % 16
     const int q = lane >> 4, j = lane & 15;
@@ -336,23 +343,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][jj],
                                                                acc[i][jj], 0, 0, 0);
     };
-    auto mma_dma = [&](int set, uint16_t *Ld, int dkt, int d0) {
+    // 16 MFMAs with DMAs d0 .. d0 + 7 of stage dkt (descriptor r) between
+    auto mma_dma = [&](int set, uint16_t *Ld, __amdgpu_buffer_rsrc_t r, int d0) {
 #pragma unroll
       for (int q = 0; q < 16; q++) {
         acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             fa[set][q >> 2], fb[set][q & 3], acc[q >> 2][q & 3], 0, 0, 0);
-        if (q & 1) dma(Ld, dkt, d0 + (q >> 1));  // zeros past the end
+        if (q & 1) dma(r, Ld, d0 + (q >> 1));  // zeros past the end
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     // `first`: stage 0, whose successor the prologue issued in full
     auto stage = [&](uint16_t *Lc, uint16_t *Ln, int kt, auto first) {
+      const __amdgpu_buffer_rsrc_t rb = desc(kt + 1, false), ra = desc(kt + 2, true);
       load(Lc, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(first)::value)
         mma(0);
       else
-        mma_dma(0, Ln, kt + 1, 8);  // second half of Ln's refill
+        mma_dma(0, Ln, rb, 8);  // second half of Ln's refill
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 1; ks < 3; ks++) {
@@ -365,16 +374,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
       __syncthreads();
       load(Ln, 0, 0);  // after the last stage this reads zeros, unused
       __builtin_amdgcn_sched_barrier(0);
-      mma_dma(1, Lc, kt + 2, 0);  // first half of Lc's refill
+      mma_dma(1, Lc, ra, 0);  // first half of Lc's refill
     };
     // Prologue: stages 0 and 1 in flight together, then the wait for stage 0
     // alone (its 16 DMAs were issued first), so a short contraction (a few
     // stages: experts with few rows) pays one memory latency up front, not
     // two.
+    {
+      const __amdgpu_buffer_rsrc_t a0 = desc(0, true), b0 = desc(0, false);
+      const __amdgpu_buffer_rsrc_t a1 = desc(1, true), b1 = desc(1, false);
 #pragma unroll
-    for (int q = 0; q < 16; q++) dma(L0, 0, q);
+      for (int q = 0; q < 16; q++) dma(q < 8 ? a0 : b0, L0, q);
 #pragma unroll
-    for (int q = 0; q < 16; q++) dma(L1, 1, q);
+      for (int q = 0; q < 16; q++) dma(q < 8 ? a1 : b1, L1, q);
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));
     barrier_after_wait();
     load(L0, 0, 0);

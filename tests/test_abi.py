@@ -4,6 +4,7 @@ argument validation) behave as documented.  No test here launches a kernel:
 every validation case returns before the library touches the device.
 """
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -141,6 +142,18 @@ def test_mx_sizes_and_shape_rules(lib):
     assert m.moe_packed_weight_bytes(mx) >= \
         m.moe_packed_weight_bytes(bf) + 2 * 3 * E * H * I * 33 // 32
     assert m.moe_workspace_bytes(m.Shape(64, 256, 8, 2, 128, 0, m.MOE_MXFP8)) > 0
+    # the MX operands' 32-bit descriptor limits: padded routed rows Rp =
+    # R + 127 E (to 128) below 2^23, Rp * max(H, 2I) below 2^36 and
+    # E * H * I below 2^35; the same shapes in bf16 are accepted
+    rp_max = m.Shape((1 << 20) - 256, 128, 8, 8, 128, 0, m.MOE_MXFP8)  # Rp = 2^23 - 1024
+    assert m.moe_workspace_bytes(rp_max) > 0
+    for big in (m.Shape(1 << 20, 128, 8, 8, 128, 0, m.MOE_MXFP8),         # Rp >= 2^23
+                m.Shape(1 << 19, 4096, 8, 8, 8192, 0, m.MOE_MXFP8),       # Rp * 2I >= 2^36
+                m.Shape(64, 16384, 1024, 2, 4096, 0, m.MOE_MXFP8)):       # E H I >= 2^35
+        assert m.moe_workspace_bytes(big) == 0, big
+        assert lib.moe_route(ctypes.byref(big.c()), 1 << 40, 1 << 40, 1 << 40, None) == \
+            _lib.MOE_ERR_UNSUPPORTED
+        assert m.moe_workspace_bytes(dataclasses.replace(big, dtype=m.MOE_BF16)) > 0
     for bad in (m.Shape(64, 192, 8, 2, 128, 0, m.MOE_MXFP8),
                 m.Shape(64, 256, 8, 2, 192, 0, m.MOE_MXFP8),
                 m.Shape(64, 256, 8, 2, 128, 64, m.MOE_MXFP8)):
