@@ -343,12 +343,12 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched,
  * pages mention a separate decode kernel for inference in which each token
  * gets its own small group of threads [NA design].  With few tokens the
  * layer is bound by reading the selected experts' weights, so the expert FFN
- * here streams each used expert's packed weight rows once, in 16-byte
- * chunks across a wave, and applies them to all of that expert's routed
- * rows (8 per pass; an expert with more rows re-reads its weights per 8),
- * with fp32 accumulation and a fixed-order lane sum (deterministic).  Meant
- * for T*k up to a few hundred rows; larger batches belong to
- * moe_layer_fwd's MFMA grouped GEMMs.  Arguments as moe_layer_fwd (x [T][H]
+ * here streams each used expert's packed weight rows once per pass, a deep
+ * ring of them in flight per wave, and applies them on the matrix cores to
+ * all of that expert's routed rows (64 per pass; an expert with more rows
+ * re-reads its weights per 64), with fp32 accumulation in a fixed order
+ * (deterministic).  Meant for T*k up to a few hundred rows; larger batches
+ * belong to moe_layer_fwd's MFMA grouped GEMMs.  Arguments as moe_layer_fwd (x [T][H]
  * bf16; router w_router/bias or supplied topk_idx/topk_w; packed from
  * moe_prepare_weights; out [T][H] bf16; ws of moe_workspace_bytes).  bf16
  * only: MXFP8 shapes return MOE_ERR_UNSUPPORTED. */

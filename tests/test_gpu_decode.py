@@ -9,8 +9,11 @@ workspace), and the decode's selection must equal the oracle's for every
 token, weights within 1e-5.  Cases: one token,
 a few tokens, a token count that is not a multiple of anything, experts with
 more than one 64-row pass (supplied routing with duplicates), unused experts,
-the shared expert, the Kimi-shaped dimensions, top-k above 8 (router and
-supplied routing), and MXFP8 shapes (refused).
+the shared expert, the Kimi-shaped dimensions (4 tokens, and 24 tokens with
+one to four 16-row blocks per pass and a second pass on the heavy expert:
+long contractions, where the weight ring wraps around its slots and a
+pass's last steps only fill it), top-k above 8 (router and supplied
+routing), and MXFP8 shapes (refused).
 """
 import numpy as np
 import pytest
@@ -46,6 +49,10 @@ CASES = {
                               router_std=1 / np.sqrt(512), hot_experts=2, hot_bias=1.0, seed=5),
     "kimi-dims-t4": synth.custom(T=4, H=7168, E=6, k=8, I=2048, zipf_s=1.0,
                                  routing="supplied", seed=6),
+    # long contractions with every row-block count: 71 rows (a 64-row pass of
+    # four blocks, then 7 rows), 44, 32, 21 and 12 rows on the experts
+    "kimi-dims-t24": synth.custom(T=24, H=7168, E=6, k=8, I=2048, zipf_s=1.0,
+                                  routing="supplied", seed=7),
     "t7-k16-router": synth.custom(T=7, H=512, E=32, k=16, I=256, routing="router",
                                   router_std=0.05, seed=14),
     "t3-k11-supplied": synth.custom(T=3, H=256, E=5, k=11, I=128, routing="supplied", seed=15),
