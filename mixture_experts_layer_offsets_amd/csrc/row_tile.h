@@ -358,11 +358,20 @@ __device__ __forceinline__ void mx_tile(const GemmArgs &p, const MxOperands &mx,
   };
   // Prologue: stages 0 and 1 (and their scales) in flight together, then
   // the wait for stage 0 and its scales alone (stage 1's 8 + NBQ DMAs and 8
-  // scale loads were issued after them): one memory latency per tile.
+  // scale loads were issued after them): one memory latency per tile.  The
+  // empty asm with a memory clobber keeps that order: without it the
+  // scheduler issued all 16 + 2 NBQ DMAs before the scale loads, the wait
+  // no longer covered stage 0's scales, and the compiler's own waits for
+  // them at the loop head then held every second stage until the DMAs
+  // issued during the stage before it had landed.
   issue(L0, 0);
   load_scales(0, sa0, sb0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   issue(L1, 1);
   load_scales(min(1, nk - 1), sa1, sb1);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(8 + NBQ + 8));
   barrier_after_wait();
   load(L0, 0, 0);
