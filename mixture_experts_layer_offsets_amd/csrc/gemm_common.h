@@ -244,6 +244,20 @@ __device__ __forceinline__ void barrier_after_wait() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left alone (vmcnt field 63,
+// expcnt 7): this wave's LDS reads and writes have completed.
+constexpr int kLgkmcnt0 = 0xC07F;
+
+// Workgroup barrier for LDS data written with ds_write: every wave's LDS
+// accesses before it have completed, its DMAs and stores may still be in
+// flight (no fence, see barrier_after_wait).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // Chunk swizzle of the DMA-fed tiles (rows of 64 bf16 = eight 16-byte

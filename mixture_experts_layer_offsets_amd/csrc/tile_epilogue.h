@@ -60,6 +60,7 @@ struct TileAt {
 // 16 chunks of one half-wave's write, in distinct banks.
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 *lds_v4i16_t;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -125,6 +126,43 @@ __device__ __forceinline__ void copy_runs_out(const uint8_t *plane, int ncol, in
         *(uint4 *)(dst + (size_t)row * ld + col) = make_uint4(l.x, l.y, h.x, h.y);
       }
     }
+  }
+}
+
+// One eighth of the SwiGLU backward's output (copy_runs_out over 32 rows x
+// 512 packed columns, 8 row quads) with exactly 8 store instructions per
+// wave whatever the valid rows and columns: a lane outside them stores to an
+// offset past the buffer descriptor, which the hardware drops.  With no
+// branch around a store the compiler counts them exactly, so a later wait
+// for older loads can leave these 8 stores in flight (vmcnt counts stores).
+__device__ __forceinline__ void copy_eighth_out(const uint8_t *plane, int rows_valid,
+                                                int col_valid, uint16_t *dst, long ld, int wave,
+                                                int lane) {
+  constexpr int ncol = 512, ncb = ncol >> 7;
+  const int g = lane >> 4, y = lane & 15;
+  const int rc = 32 * g + 8 * (y & 3) + (y >> 2);  // column this lane addresses
+  const int oc = 32 * g + 8 * (y >> 2), orow = y & 3;  // what it receives
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void *)dst, (short)0, 0x7FFFFFFF, kBufferDword3);
+  v4i16 lo[8], hi[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int u = wave + 4 * k, q = u / ncb, cb = (u - q * ncb) << 7;
+    lo[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t)(plane + run_off(q, cb + rc, ncol)));
+    hi[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t)(plane + run_off(q, cb + rc + 4, ncol)));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int u = wave + 4 * k, q = u / ncb, cb = (u - q * ncb) << 7;
+    const int row = 4 * q + orow, col = cb + oc;
+    const uint32_t off = row < rows_valid && col < col_valid
+                             ? (uint32_t)((row * ld + col) * 2)
+                             : 0x80000000u;
+    const uint2 l = __builtin_bit_cast(uint2, lo[k]), h = __builtin_bit_cast(uint2, hi[k]);
+    const v4u32 v = {l.x, l.y, h.x, h.y};
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, (int)off, 0, 0);
   }
 }
 
@@ -282,6 +320,13 @@ __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
   const uint16_t *gu_base = p.aux + (size_t)(t.rowbase + t.m0) * p.ldaux + 2L * t.n0;
   uint16_t *out_base = (uint16_t *)p.C + (size_t)(t.rowbase + t.m0) * p.ldc + 2L * t.n0;
   auto rows_of = [&](int e) { return min(32, t.Mg - t.m0 - 32 * e); };
+  // Q[e & 1] holds eighth e's g|u rows: the even eighths in L1, the odd ones
+  // in an LDS object of their own (32 KB more, 160 KB in all).  The compiler
+  // waits for the DMAs into an LDS object before reading it, so with both
+  // halves in L1 every read of eighth e also waited for eighth e + 1's DMA,
+  // issued just before.
+  __shared__ __attribute__((aligned(1024))) uint8_t q_odd[kBwdRegion];
+  auto q_of = [&](int e) { return (e & 1) ? q_odd : L1; };
   // g|u rows of eighth e into Q[e & 1] (rows past the tile read as zeros)
   auto dma = [&](int e) {
     const int rv = rows_of(e);
@@ -289,7 +334,7 @@ __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(gu_base + (size_t)32 * e * p.ldaux), (short)0, rv * (int)p.ldaux * 2,
         kBufferDword3);
-    uint8_t *Q = L1 + (e & 1) * kBwdRegion;
+    uint8_t *Q = q_of(e);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       const int r = wave * 8 + k;
@@ -298,21 +343,28 @@ __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
           (uint32_t)(r * (int)p.ldaux * 2 + ((lane ^ ((r & 3) << 1)) << 4)), 0, 0, 0);
     }
   };
+  // 8 store instructions per wave, also for rows past the tile (dropped)
   auto copy_out = [&](int e) {
-    const int rv = rows_of(e);
-    if (rv > 0)
-      copy_runs_out(L0 + (e & 1) * kBwdRegion, 512, 8, rv, span_cols,
+    copy_eighth_out(L0 + (e & 1) * kBwdRegion, max(rows_of(e), 0), span_cols,
                     out_base + (size_t)32 * e * p.ldc, p.ldc, wave, lane);
   };
+  // The barriers below are lds_barrier: __syncthreads' fence would also wait
+  // for the next eighth's g|u DMA (issued just before) and the previous
+  // eighth's stores, every eighth.  Only the wait at the top of an eighth
+  // waits for memory: for this wave's DMA of the eighth's rows, which was
+  // followed only by the 8 stores of copy_out(e - 2), which stay in flight.
   __syncthreads();  // the operand buffers are free
   dma(0);
 #pragma unroll
   for (int e = 0; e < 8; e++) {
     uint8_t *P = L0 + (e & 1) * kBwdRegion;
-    const uint8_t *Q = L1 + (e & 1) * kBwdRegion;
+    const uint8_t *Q = q_of(e);
     const int rv = rows_of(e);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // eighth e's rows (and older stores)
-    __syncthreads();
+    if (e >= 2)  // (e is a constant once the loop is unrolled)
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(8));  // eighth e's rows
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    lds_barrier();
     if (e + 1 < 8) dma(e + 1);  // Q[(e + 1) & 1] was last read by eighth e - 1
     if (rv > 0 && t.wm0 == 128 * (e >> 2)) {
       const int i = e & 3, qh = lane >> 5;
@@ -326,7 +378,7 @@ __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
                           acc[i][j][4 * vq + 3]);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // runs: wave w takes units w, w + 4 (8 each): row quad u / 4, 64 columns
     // (u % 4) * 64, group g their 16 columns from 16 g
     uint2 og[8], ou[8];
@@ -356,7 +408,7 @@ __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
       }
     }
     if (e > 0) copy_out(e - 1);
-    __syncthreads();  // every dA run of eighth e has been read
+    lds_barrier();  // every dA run of eighth e has been read
     if (rv > 0) {
 #pragma unroll
       for (int k = 0; k < 8; k++) {
@@ -367,7 +419,7 @@ __device__ __forceinline__ void tile_epi_swiglu_bwd(const GemmArgs &p,
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   copy_out(7);
 }
 
