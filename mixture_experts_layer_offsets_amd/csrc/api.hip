@@ -474,27 +474,29 @@ void gemm_dgrad_gate_up(const uint16_t *dh, MxT dhq, const int32_t *offsets, con
   }
 }
 
+// `rows`: the rows over the groups (at most).
 void gemm_wgrad_down(const uint16_t *act, const uint16_t *dY, const int32_t *offsets,
-                     const int32_t *order, int G, long H, long I, float *dWd, hipStream_t s) {
+                     const int32_t *order, int G, long rows, long H, long I, float *dWd,
+                     hipStream_t s) {
   GemmArgs b{};
   b.A = act; b.lda = I;
   b.B = dY; b.ldb = H;
   b.C = dWd; b.ldc = H; b.sC = I * H;
   b.offsets = offsets; b.order = order;
   b.G = G; b.M = (int)I; b.N = (int)H;
-  launch_gemm_wgrad(b, EPI_F32, s);
+  launch_gemm_wgrad(b, EPI_F32, rows, s);
 }
 
 void gemm_wgrad_gate_up(const uint16_t *X, const uint16_t *dh, const int32_t *offsets,
-                        const int32_t *order, int G, long H, long I, float *dWg, float *dWu,
-                        hipStream_t s) {
+                        const int32_t *order, int G, long rows, long H, long I, float *dWg,
+                        float *dWu, hipStream_t s) {
   GemmArgs e{};
   e.A = X; e.lda = H;
   e.B = dh; e.ldb = 2 * I;
   e.C = dWg; e.C2 = dWu; e.ldc = I; e.sC = H * I;
   e.offsets = offsets; e.order = order;
   e.G = G; e.M = (int)H; e.N = (int)(2 * I);
-  launch_gemm_wgrad(e, EPI_WGRAD_GU, s);
+  launch_gemm_wgrad(e, EPI_WGRAD_GU, rows, s);
 }
 
 // MX weight gradients: both operands quantised down the rows per expert
@@ -536,17 +538,17 @@ void gemm_wgrad_gate_up_mx(const uint16_t *X, const uint16_t *dh, const int32_t 
 
 // Either weight-gradient form (mxw == nullptr: bf16).
 void wgrad_down_any(const uint16_t *act, const uint16_t *dY, const int32_t *offsets,
-                    const int32_t *order, int G, long H, long I, float *dWd, const MxWgrad *mxw,
-                    hipStream_t s) {
+                    const int32_t *order, int G, long rows, long H, long I, float *dWd,
+                    const MxWgrad *mxw, hipStream_t s) {
   if (mxw) gemm_wgrad_down_mx(act, dY, offsets, order, G, H, I, dWd, *mxw, s);
-  else gemm_wgrad_down(act, dY, offsets, order, G, H, I, dWd, s);
+  else gemm_wgrad_down(act, dY, offsets, order, G, rows, H, I, dWd, s);
 }
 
 void wgrad_gate_up_any(const uint16_t *X, const uint16_t *dh, const int32_t *offsets,
-                       const int32_t *order, int G, long H, long I, float *dWg, float *dWu,
-                       const MxWgrad *mxw, hipStream_t s) {
+                       const int32_t *order, int G, long rows, long H, long I, float *dWg,
+                       float *dWu, const MxWgrad *mxw, hipStream_t s) {
   if (mxw) gemm_wgrad_gate_up_mx(X, dh, offsets, order, G, H, I, dWg, dWu, *mxw, s);
-  else gemm_wgrad_gate_up(X, dh, offsets, order, G, H, I, dWg, dWu, s);
+  else gemm_wgrad_gate_up(X, dh, offsets, order, G, rows, H, I, dWg, dWu, s);
 }
 
 // The whole expert-FFN backward over row-ragged groups, given dY (rows'
@@ -560,12 +562,12 @@ void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
   if (mx) launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
   gemm_dgrad_down(dY, dyq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, gu_saved, dh, s);
   if (st) st->mark(mark);
-  wgrad_down_any(act, dY, offsets, order, G, H, I, dWd, mxw, s);
+  wgrad_down_any(act, dY, offsets, order, G, max_rows, H, I, dWd, mxw, s);
   if (st) st->mark(mark + 1);
   if (mx) launch_quant_rows_mx(dh, (int)max_rows, (int)(2 * I), dhq.q, dhq.s, s);
   gemm_dgrad_gate_up(dh, dhq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, dX, s);
   if (st) st->mark(mark + 2);
-  wgrad_gate_up_any(X, dh, offsets, order, G, H, I, dWg, dWu, mxw, s);
+  wgrad_gate_up_any(X, dh, offsets, order, G, max_rows, H, I, dWg, dWu, mxw, s);
   if (st) st->mark(mark + 3);
 }
 
@@ -957,9 +959,10 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   const MxWgrad mxw{w.poff, w.Rp, w.wq_a, w.wq_b};
   const MxWgrad *pm = (d.mx && sc->mx_wgrad) ? &mxw : nullptr;
   if (pm) launch_pad_offsets(sv.offsets, E, w.poff, q);
-  wgrad_down_any(sv.act, w.dy, sv.offsets, sv.order, E, d.H, d.I, dw_down, pm, q);
+  wgrad_down_any(sv.act, w.dy, sv.offsets, sv.order, E, d.R, d.H, d.I, dw_down, pm, q);
   if (!c.wait(q, evDD)) return MOE_ERR_HIP;
-  wgrad_gate_up_any(sv.x_perm, w.dh, sv.offsets, sv.order, E, d.H, d.I, dw_gate, dw_up, pm, q);
+  wgrad_gate_up_any(sv.x_perm, w.dh, sv.offsets, sv.order, E, d.R, d.H, d.I, dw_gate, dw_up, pm,
+                    q);
   if (!c.join(evX + 1)) return MOE_ERR_HIP;
   return hip_status();
 }

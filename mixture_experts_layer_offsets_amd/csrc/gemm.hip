@@ -251,8 +251,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
   const int per = p.n_tiles_m * p.n_tiles_n;
-  const int gi = blockIdx.x / per;
-  const int rem = blockIdx.x - gi * per;
+  // Workgroup b runs on XCD b % 8.  In XCD-major order (p.xcd_major, see
+  // launch_gemm_wgrad) XCD x takes all tiles of groups x, x + 8, ... in
+  // row-major order, so each group's operand rows are read by one XCD and
+  // shared in its L2 by its concurrent tiles; in the plain order a tile's
+  // column index picks its XCD and every XCD fetches every group's A panel.
+  int gi, rem;
+  if (p.xcd_major) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3, q = j / per;
+    gi = q * 8 + x;
+    rem = j - q * per;
+  } else {
+    gi = blockIdx.x / per;
+    rem = blockIdx.x - gi * per;
+  }
   const int g = p.order ? p.order[gi] : gi;
   const int mt = rem / p.n_tiles_n;
   const int m0 = mt * BM, n0 = (rem - mt * p.n_tiles_n) * BN;
@@ -438,13 +450,20 @@ void launch_gemm_rows(const GemmArgs &p0, int epi, bool b_kcontig, int max_rows,
   else launch_epi<false, false>(p, epi, (int)grid, s);
 }
 
-void launch_gemm_wgrad(const GemmArgs &p0, int epi, hipStream_t s) {
+void launch_gemm_wgrad(const GemmArgs &p0, int epi, long rows, hipStream_t s) {
   GemmArgs p = p0;
   p.stamps = current_stamps();
   p.n_tiles_m = (p.M + BM - 1) / BM;
   p.n_tiles_n = (p.N + BN - 1) / BN;
   const long grid = (long)p.G * p.n_tiles_m * p.n_tiles_n;
   if (grid <= 0) return;
+  // XCD-major tile order when the groups are many (a multiple of 8, so every
+  // XCD gets as many) and an average group's operand rows, rows / G x (M + N)
+  // bf16 values, fit one XCD's 4 MB L2, so that each XCD reads them once.
+  // Measured: the 64-expert mid layer's weight gradients 4-6 % faster; with
+  // the DeepSeek-V3 share's larger groups (4.7 and 5.8 MB) the down one was
+  // 2 % faster and the gate/up one 8 % slower.
+  p.xcd_major = p.G % 8 == 0 && p.G >= 16 && rows / p.G * (long)(p.M + p.N) * 2 <= (4L << 20);
   if (p.lda % 8 == 0 && p.ldb % 8 == 0 && p.lda >= BM && p.ldb >= BN &&
       (epi == EPI_F32 || epi == EPI_WGRAD_GU)) {
     const dim3 gr((unsigned)grid), b(NT);

@@ -117,6 +117,7 @@ struct GemmArgs {
   const int32_t *order;       // [G] group processing order (weight-gradient mode)
   int G, M, N, K;
   int n_tiles_m, n_tiles_n;
+  int xcd_major;  // weight-gradient mode: XCD-major tile order (gemm_tn_kernel)
   unsigned long long *stamps;  // optional per-tile timing counters (TileClock)
 };
 
@@ -195,6 +196,8 @@ void launch_gemm_mx_wgrad(const GemmArgs &p, const MxOperands &mx, int epi, hipS
 // Weight-gradient grouped GEMM: for group g, C_g[M][N] = sum over rows
 // [offsets[g], offsets[g+1]) of A[row][M]^T B[row][N] (both row-major with the
 // summed rows outermost).
-void launch_gemm_wgrad(const GemmArgs &p, int epi, hipStream_t s);
+// Weight gradients C_g = A_g^T B_g over the groups' row ranges; `rows`: the
+// rows over all groups (at most), which picks the tile order.
+void launch_gemm_wgrad(const GemmArgs &p, int epi, long rows, hipStream_t s);
 
 }  // namespace moe
