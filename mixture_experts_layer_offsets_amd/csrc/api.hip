@@ -1411,12 +1411,12 @@ int moe_decode_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_
     launch_layout(idx, (int)d.R, E, w.chunk_counts, w.dec_counts, w.dec_offsets, w.dec_perm,
                   w.dec_inv, w.tile_start, kTileM, w.order, s);
   // routed experts: rows grouped by expert, x gathered through perm
-  launch_decode_ffn(x, w.dec_perm, w.dec_offsets, E, k, H, (int)d.I, p.r.guT, p.r.dT, w.act,
-                    w.dX, s);
+  launch_decode_ffn(x, w.dec_perm, w.dec_offsets, E, d.R, k, H, (int)d.I, p.r.guT, p.r.dT,
+                    w.act, w.dX, s);
   if (d.shared) {
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
-    launch_decode_ffn(x, nullptr, w.dense_offsets, 1, 1, H, (int)d.Is, p.s.guT, p.s.dT, w.dh_s,
-                      w.dxs, s);
+    launch_decode_ffn(x, nullptr, w.dense_offsets, 1, T, 1, H, (int)d.Is, p.s.guT, p.s.dT,
+                      w.dh_s, w.dxs, s);
   }
   launch_combine(w.dX, wts, w.dec_inv, d.shared ? w.dxs : nullptr, out, T, k, H, s);
   return hip_status();

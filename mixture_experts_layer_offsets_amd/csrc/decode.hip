@@ -38,6 +38,7 @@
 // its own DMA lane wrote, so the wave needs no barrier.  Steps past the end
 // still issue (a zero-byte weight load, a row reload of step 0) so every
 // wait has a fixed count; their MFMAs are skipped.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(64) void decode_gate_up_kernel(
 #pragma unroll
   for (int m = 0; m < kDecTiles; m++)
     wo[m] = (uint32_t)((32 * m + (lane & 15)) * H * 2 + (lane >> 4) * 16);
-  for (int r0 = rb; r0 < re; r0 += kDecRows) {
+  for (int r0 = rb + blockIdx.z * kDecRows; r0 < re; r0 += gridDim.z * kDecRows) {
     const int nr = min(kDecRows, re - r0), nb = (nr + 15) / 16;
     const uint4 *xrow[kDecRowBlocks];
 #pragma unroll
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(64) void decode_down_kernel(const uint16_t *act,
 #pragma unroll
   for (int m = 0; m < kDecTiles; m++)
     wo[m] = (uint32_t)((16 * m + (lane & 15)) * I * 2 + (lane >> 4) * 16);
-  for (int r0 = rb; r0 < re; r0 += kDecRows) {
+  for (int r0 = rb + blockIdx.z * kDecRows; r0 < re; r0 += gridDim.z * kDecRows) {
     const int nr = min(kDecRows, re - r0), nb = (nr + 15) / 16;
     const uint4 *xrow[kDecRowBlocks];
 #pragma unroll
@@ -331,15 +332,19 @@ void launch_decode_layout(const int32_t *idx, int R, int E, int32_t *counts, int
 }
 
 void launch_decode_ffn(const uint16_t *x, const int32_t *perm, const int32_t *offsets, int G,
-                       int k, int H, int I, const uint16_t *guT, const uint16_t *dT,
+                       long rows, int k, int H, int I, const uint16_t *guT, const uint16_t *dT,
                        uint16_t *act, uint16_t *y, hipStream_t s) {
-  if (G <= 0) return;
+  if (G <= 0 || rows <= 0) return;
   // one wave per 16 intermediate indices (gate/up) or 32 hidden indices
-  // (down); H and I are multiples of 64
-  hipLaunchKernelGGL(decode_gate_up_kernel, dim3(I / 16, G), dim3(64), 0, s, x, perm, offsets,
-                     guT, act, k, H, I);
-  hipLaunchKernelGGL(decode_down_kernel, dim3(H / 32, G), dim3(64), 0, s, act, offsets, dT, y, H,
-                     I);
+  // (down) and per 64-row pass (grid z: enough passes for a group holding all
+  // `rows`; a wave past its group's last pass exits at once), so the passes
+  // of a group with many rows run side by side instead of one after another
+  // in the same waves; H and I are multiples of 64
+  const unsigned passes = (unsigned)std::min<long>((rows + kDecRows - 1) / kDecRows, 65535);
+  hipLaunchKernelGGL(decode_gate_up_kernel, dim3(I / 16, G, passes), dim3(64), 0, s, x, perm,
+                     offsets, guT, act, k, H, I);
+  hipLaunchKernelGGL(decode_down_kernel, dim3(H / 32, G, passes), dim3(64), 0, s, act, offsets,
+                     dT, y, H, I);
 }
 
 }  // namespace moe

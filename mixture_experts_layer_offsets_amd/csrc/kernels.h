@@ -85,9 +85,10 @@ void launch_reverse_dispatch_list(const uint16_t *dX, const int32_t *inv, const 
 // decode.hip: few-token expert FFN (weight-streaming GEMV form).  For each of
 // G groups (experts; offsets [G+1]) and its rows r: act[r] = silu(x[t] Wg) *
 // (x[t] Wu), y[r] = act[r] Wd, t = perm[r] / k (perm == nullptr: t = r).
-// guT: packed gate/up [G][2I][H]; dT: packed down [G][H][I].
+// guT: packed gate/up [G][2I][H]; dT: packed down [G][H][I].  `rows`: the
+// rows over all groups (bounds the rows of one group).
 void launch_decode_ffn(const uint16_t *x, const int32_t *perm, const int32_t *offsets, int G,
-                       int k, int H, int I, const uint16_t *guT, const uint16_t *dT,
+                       long rows, int k, int H, int I, const uint16_t *guT, const uint16_t *dT,
                        uint16_t *act, uint16_t *y, hipStream_t s);
 // The layer's layout (counts, offsets, perm, inv; same result as
 // launch_layout) in one workgroup, for R <= kDecLayoutMax routed rows.
