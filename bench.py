@@ -55,9 +55,9 @@ MX_GEMMS = ("gemm_gate_up_swiglu", "gemm_down", "gemm_dgrad_down_swiglu_bwd",
 CSRC = os.path.join(ROOT, "mixture_experts_layer_offsets_amd", "csrc")
 KERNEL_SOURCES = {
     "gemm_nt_kernel<2>": ("gemm.hip", "gemm_common.h", "row_tile.h", "tile_epilogue.h",
-                          "kernels.h", "common.h"),
+                          "tile_order.h", "kernels.h", "common.h"),
     "gemm_mx_kernel<2, 0>": ("gemm_mx.hip", "gemm_common.h", "mx_device.h", "row_tile.h",
-                             "tile_epilogue.h", "kernels.h", "common.h"),
+                             "tile_epilogue.h", "tile_order.h", "kernels.h", "common.h"),
 }
 
 FWD_STAGES = ["route+layout", "dispatch", "gemm_gate_up_swiglu", "gemm_down", "shared",

@@ -251,20 +251,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_tn_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
   const int per = p.n_tiles_m * p.n_tiles_n;
-  // Workgroup b runs on XCD b % 8.  In XCD-major order (p.xcd_major, see
-  // launch_gemm_wgrad) XCD x takes all tiles of groups x, x + 8, ... in
-  // row-major order, so each group's operand rows are read by one XCD and
-  // shared in its L2 by its concurrent tiles; in the plain order a tile's
-  // column index picks its XCD and every XCD fetches every group's A panel.
-  int gi, rem;
-  if (p.xcd_major) {
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3, q = j / per;
-    gi = q * 8 + x;
-    rem = j - q * per;
-  } else {
-    gi = blockIdx.x / per;
-    rem = blockIdx.x - gi * per;
-  }
+  int gi, rem;  // plain or XCD-major order (tile_order.h, launch_gemm_wgrad)
+  wgrad_tile_of_block(blockIdx.x, per, p.xcd_major != 0, gi, rem);
   const int g = p.order ? p.order[gi] : gi;
   const int mt = rem / p.n_tiles_n;
   const int m0 = mt * BM, n0 = (rem - mt * p.n_tiles_n) * BN;

@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "tile_order.h"
 
 namespace moe {
 
@@ -174,24 +175,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, f32x16 (&acc)[4][4],
       }
     }
   }
-}
-
-// Tile of a row-ragged GEMM for workgroup b (MT row tiles x nN column tiles,
-// b < MT nN).  Workgroups go to the eight XCDs in turn (b mod 8), so each
-// XCD runs 32 of every 256 consecutive workgroups at once; the remap hands
-// those 32 a compact block of 4 row tiles x 8 column tiles, taken from bands
-// of 8 column tiles (row tiles fastest across blocks), so a row panel is
-// read by one XCD's L2 instead of by all eight.  Full rounds of 256 are
-// permuted; a last partial round keeps the band order.  Measured on MI355X:
-// up to 5 % faster for 8 column tiles (with the plain n-fastest order each
-// XCD then holds one column and 32 row panels), neutral for 16 and 28.
-__device__ __forceinline__ void tile_of_block(int b, int MT, int nN, int &mt, int &nt) {
-  const int total = MT * nN, full = total & ~255;
-  const int k = b < full ? ((((b >> 8) << 3) + (b & 7)) << 5) + ((b & 255) >> 3) : b;
-  const int nb = (nN + 7) >> 3, per = MT << 3;
-  const int beta = min(k / per, nb - 1), kk = k - beta * per, w = min(8, nN - (beta << 3));
-  mt = kk / w;
-  nt = (beta << 3) + kk - (kk / w) * w;
 }
 
 // In-kernel timing of one tile (kernels.h, kStamp*): read only when the
