@@ -165,13 +165,20 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t *__rest
 // never straddles two experts).  The stage's rows of the 64 columns (zeros
 // past the expert's rows) are loaded with 16-byte row-wise loads into LDS;
 // then wave q converts 32-row block q, one column per lane, reading LDS
-// row-wise (conflict-free), and writes the block's 32 codes to q[c] and its
-// scale byte -- the four waves together fill each column's 128-byte line.
+// row-wise (conflict-free), writes the block's scale byte and puts its 32
+// codes into the column's 128-byte line, staged in LDS; the lines leave as
+// 16-byte stores, eight lanes per line, so each store instruction writes
+// eight whole lines (storing the 32 codes straight from the converting lane
+// split every line into 16-byte pieces from different instructions).
 __global__ __launch_bounds__(256) void quant_cols_mx_kernel(
     const uint16_t *__restrict__ src, int C, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ poff, int E, long Rp, uint8_t *__restrict__ q,
     uint8_t *__restrict__ sc) {
   __shared__ uint4 tile[MXK][8];  // 128 rows x 64 bf16
+  // column j's 128 codes at byte 144 j: the 16-byte pad puts the 64 lanes'
+  // writes of one block (stride 144) on distinct banks
+  constexpr int kLine = MXK + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lines[64 * kLine];
   const int c0 = blockIdx.x * 64;
   const int st = blockIdx.y, kp = st * MXK;
   if (kp >= poff[E]) return;  // uniform over the workgroup
@@ -191,17 +198,26 @@ __global__ __launch_bounds__(256) void quant_cols_mx_kernel(
   }
   __syncthreads();
   const int blk = tid >> 6, j = tid & 63, c = c0 + j;
-  if (c >= C) return;
-  const uint16_t *t16 = (const uint16_t *)tile;
-  float v[32];
+  {
+    const uint16_t *t16 = (const uint16_t *)tile;
+    float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; i++) v[i] = bf16_to_f32(t16[(32 * blk + i) * 64 + j]);
-  uint32_t w[8];
-  const uint32_t s = mx_block32(v, w, nullptr);
-  uint4 *dst = (uint4 *)(q + (size_t)c * Rp + kp + 32 * blk);
-  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  sc[((size_t)st * C + c) * 4 + blk] = (uint8_t)s;
+    for (int i = 0; i < 32; i++) v[i] = bf16_to_f32(t16[(32 * blk + i) * 64 + j]);
+    uint32_t w[8];
+    const uint32_t s = mx_block32(v, w, nullptr);
+    uint4 *ln = (uint4 *)(lines + j * kLine + 32 * blk);
+    ln[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    ln[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if (c < C) sc[((size_t)st * C + c) * 4 + blk] = (uint8_t)s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int piece = tid + 256 * i, col = piece >> 3, part = piece & 7;
+    if (c0 + col < C)
+      *(uint4 *)(q + (size_t)(c0 + col) * Rp + kp + 16 * part) =
+          *(const uint4 *)(lines + col * kLine + 16 * part);
+  }
 }
 
 // One 256 x 256 tile of expert order[gi]'s weight gradient C_e[M][N] =
