@@ -136,8 +136,10 @@ def _algorithmic(w):
         "dispatch": T * H * 2 + R * H * xb + R * 4,
         # routed rows read once, token rows written once, + weights/indices
         "combine": R * H * 2 + T * H * 2 + R * 8,
-        # dOut read once, Y read for dw, dY written, + weights/indices/dw
-        "reverse_combine": T * H * 2 + 2 * R * H * 2 + R * 12,
+        # dOut read once, Y read for dw, dY written, + weights/indices/dw;
+        # with MXFP8 also dY's codes and scales (the down data gradient's operand)
+        "reverse_combine": T * H * 2 + 2 * R * H * 2 + R * 12
+        + (R * H * (1.0 + 1.0 / 32) if w.mx else 0.0),
     }
     if w.routing == "supplied":
         # without a router this stage is reverse-dispatch alone: the rows'

@@ -558,8 +558,8 @@ void ffn_backward(const uint16_t *X, const uint16_t *dY, const int32_t *offsets,
                   long I, const WSet &W, bool mx, MxT dyq, MxT dhq, const uint16_t *gu_saved,
                   const uint16_t *act, uint16_t *dh, uint16_t *dX, float *dWg, float *dWu,
                   float *dWd, hipStream_t s, const Stages *st = nullptr, int mark = 0,
-                  const MxWgrad *mxw = nullptr) {
-  if (mx) launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
+                  const MxWgrad *mxw = nullptr, bool dy_quantised = false) {
+  if (mx && !dy_quantised) launch_quant_rows_mx(dY, (int)max_rows, (int)H, dyq.q, dyq.s, s);
   gemm_dgrad_down(dY, dyq, offsets, tiles, G, max_rows, max_rows, H, I, W, mx, gu_saved, dh, s);
   if (st) st->mark(mark);
   wgrad_down_any(act, dY, offsets, order, G, max_rows, H, I, dWd, mxw, s);
@@ -921,7 +921,8 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
   auto rows_of = [&](int m) { return (int)std::min(MB, d.R - (long)m * MB); };
   auto RC = [&](int m) {
     launch_reverse_combine_rows(dout, sv.y, sv.w, sv.perm, w.dy, dw, (int)(m * MB), rows_of(m), k,
-                                H, r->comm);
+                                H, d.mx ? w.dyq.q : nullptr, d.mx ? w.dyq.s : nullptr, R,
+                                r->comm);
     return c.rec(r->comm, evRC + m);
   };
   const int evDD = 2 * NM + 4;  // dgrad-down of the walk's last minibatch
@@ -929,7 +930,6 @@ int pipe_backward(const Dims &d, const moe_sched *sc, const uint16_t *dout, cons
     const int r0 = (int)(m * MB), n = rows_of(m);
     const int32_t *mo = w.pm_off + (size_t)m * (E + 1), *mt = w.pm_ts + (size_t)m * (E + 1);
     if (!c.wait(q, evRC + m)) return false;
-    if (d.mx) launch_quant_rows_mx_range(w.dy, r0, n, R, H, w.dyq.q, w.dyq.s, q);
     gemm_dgrad_down(w.dy, w.dyq, mo, mt, E, n, d.R, d.H, d.I, p.r, d.mx, sv.gu, w.dh, q);
     if (m == 0 && !c.rec(q, evDD)) return false;
     if (d.mx) launch_quant_rows_mx_range(w.dh, r0, n, R, (int)(2 * d.I), w.dhq.q, w.dhq.s, q);
@@ -1338,7 +1338,7 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
 
   // Reverse-combine: dY rows, dw, and (router) the selected-logit gradient
   launch_reverse_combine(dout, sv.y, sv.w, sv.inv, w.dy, dw, router ? w.dsel : nullptr, T, k, H,
-                         s);
+                         d.mx ? w.dyq.q : nullptr, d.mx ? w.dyq.s : nullptr, s);
   st.mark(1);
   // Expert FFN backward
   const bool mxw_on = d.mx && sched && sched->mx_wgrad;
@@ -1346,7 +1346,7 @@ int moe_layer_bwd(const moe_shape *shape, const moe_sched *sched, const uint16_t
   if (mxw_on) launch_pad_offsets(sv.offsets, E, w.poff, s);
   ffn_backward(sv.x_perm, w.dy, sv.offsets, sv.tile_start, sv.order, E, d.R, d.H, d.I, p.r,
                d.mx, w.dyq, w.dhq, sv.gu, sv.act, w.dh, w.dX, dw_gate, dw_up, dw_down, s, &st,
-               2, mxw_on ? &mxw : nullptr);
+               2, mxw_on ? &mxw : nullptr, /*dy_quantised=*/true);
   if (d.shared) {
     launch_dense_groups(w.dense_offsets, w.dense_tiles, w.dense_order, T, kTileM, s);
     float *dWsg = dws, *dWsu = dws + d.H * d.Is, *dWsd = dws + 2 * d.H * d.Is;

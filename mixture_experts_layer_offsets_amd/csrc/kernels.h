@@ -52,9 +52,11 @@ void launch_quant_rows_mx_range(const uint16_t *src, int row0, int rows, int row
                                 uint8_t *q, uint8_t *sc, hipStream_t s);
 void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const uint16_t *ys,
                     uint16_t *out, int T, int k, int H, hipStream_t s);
+// dyq/dys non-null (MXFP8): dY is also written as E4M3 codes [T k][H] and
+// K-blocked E8M0 scales, exactly as launch_quant_rows_mx would make them.
 void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float *w,
                             const int32_t *inv, uint16_t *dy, float *dw, float *dsel, int T,
-                            int k, int H, hipStream_t s);
+                            int k, int H, uint8_t *dyq, uint8_t *dys, hipStream_t s);
 void launch_reverse_dispatch(const uint16_t *dX, const int32_t *inv, const int32_t *idx,
                              const float *dsel, const uint16_t *wrT, const uint16_t *dxs,
                              uint16_t *dx, int T, int k, int H, hipStream_t s);
@@ -75,7 +77,8 @@ void launch_combine_list(const uint16_t *y, const float *w, const int32_t *inv,
                          const int32_t *tl_off, int m, int T, int k, int H, hipStream_t s);
 void launch_reverse_combine_rows(const uint16_t *dout, const uint16_t *y, const float *w,
                                  const int32_t *perm, uint16_t *dy, float *dw, int r0, int rows,
-                                 int k, int H, hipStream_t s);
+                                 int k, int H, uint8_t *dyq, uint8_t *dys, long rows_total,
+                                 hipStream_t s);
 void launch_reverse_dispatch_list(const uint16_t *dX, const int32_t *inv, const int32_t *idx,
                                   const float *w, const float *dw, float *dsel,
                                   const uint16_t *wrT, const uint16_t *dxs, uint16_t *dx,

@@ -87,4 +87,16 @@ __device__ __forceinline__ uint32_t mx_quad8(const float *v, uint2 *codes, float
   return (uint32_t)(s + 127);
 }
 
+// One 8-value chunk of a row in the row quantiser's output form (the four
+// lanes of a quad hold one 32-value block and must all be active): E4M3
+// codes at chunk c of row `row` (HC chunks per row), the block's E8M0 scale
+// K-blocked, block b = c/4 at byte (b/4 * rows_total + row) * 4 + b%4.
+__device__ __forceinline__ void mx_put_chunk(const float *v, long row, int c, int HC,
+                                             long rows_total, uint2 *q, uint8_t *s) {
+  uint2 codes;
+  const uint32_t sc = mx_quad8(v, &codes, nullptr);
+  q[(size_t)row * HC + c] = codes;
+  if ((c & 3) == 0) s[((size_t)(c >> 4) * rows_total + row) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
+}
+
 }  // namespace moe

@@ -266,15 +266,19 @@ void launch_combine(const uint16_t *y, const float *w, const int32_t *inv, const
 // the slot weight, and dw[t,j] = <dout[t], y[row]>.  With a router, also the
 // selected-logit gradient dsel[t,j] = w_j (dw_j - sum_j' w_j' dw_j').
 // One 256-thread block per token; the dot products reduce in a fixed tree.
+// With MXFP8 (MXQ) each dY chunk is also written in the row quantiser's form
+// (codes and K-blocked scales of the stored bf16 values), the down data
+// gradient's operand, so dY is not read back to quantise it.
 
 constexpr int kMaxTopK = 16;
 
 // KMAX bounds k (see combine8): 8 for k <= 8, else kMaxTopK.
-template <int KMAX>
+template <int KMAX, bool MXQ>
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const uint4 *__restrict__ dout, const uint4 *__restrict__ y, const float *__restrict__ w,
     const int32_t *__restrict__ inv, uint4 *__restrict__ dy, float *__restrict__ dw,
-    float *__restrict__ dsel, int k, int HC) {
+    float *__restrict__ dsel, int k, int HC, uint2 *__restrict__ dyq, uint8_t *__restrict__ dys,
+    long rows_total) {
   __shared__ float red[KMAX][4];
   const int t = blockIdx.x, tid = threadIdx.x;
   float part[KMAX];
@@ -321,7 +325,13 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
             o[q] = wt[j] * d[q];
           }
           part[j] += s;
-          dy[(size_t)rows[j] * HC + c] = pack8(o);
+          const uint4 pk = pack8(o);
+          dy[(size_t)rows[j] * HC + c] = pk;
+          if constexpr (MXQ) {  // a quad's lanes share j, u and the guards
+            float vq[8];
+            unpack8(pk, vq);
+            mx_put_chunk(vq, rows[j], c, HC, rows_total, dyq, dys);
+          }
         }
       }
     }
@@ -347,15 +357,26 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
 
 void launch_reverse_combine(const uint16_t *dout, const uint16_t *y, const float *w,
                             const int32_t *inv, uint16_t *dy, float *dw, float *dsel, int T,
-                            int k, int H, hipStream_t s) {
+                            int k, int H, uint8_t *dyq, uint8_t *dys, hipStream_t s) {
   if (T <= 0) return;
-  if (k <= 8)
-    hipLaunchKernelGGL(reverse_combine_kernel<8>, dim3(T), dim3(256), 0, s, (const uint4 *)dout,
-                       (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k, H / 8);
-  else
-    hipLaunchKernelGGL(reverse_combine_kernel<kMaxTopK>, dim3(T), dim3(256), 0, s,
+  const long R = (long)T * k;
+  uint2 *q = (uint2 *)dyq;
+  if (k <= 8 && dyq)
+    hipLaunchKernelGGL((reverse_combine_kernel<8, true>), dim3(T), dim3(256), 0, s,
                        (const uint4 *)dout, (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k,
-                       H / 8);
+                       H / 8, q, dys, R);
+  else if (k <= 8)
+    hipLaunchKernelGGL((reverse_combine_kernel<8, false>), dim3(T), dim3(256), 0, s,
+                       (const uint4 *)dout, (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k,
+                       H / 8, q, dys, R);
+  else if (dyq)
+    hipLaunchKernelGGL((reverse_combine_kernel<kMaxTopK, true>), dim3(T), dim3(256), 0, s,
+                       (const uint4 *)dout, (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k,
+                       H / 8, q, dys, R);
+  else
+    hipLaunchKernelGGL((reverse_combine_kernel<kMaxTopK, false>), dim3(T), dim3(256), 0, s,
+                       (const uint4 *)dout, (const uint4 *)y, w, inv, (uint4 *)dy, dw, dsel, k,
+                       H / 8, q, dys, R);
 }
 
 // ---------------------------------------------------------------------------

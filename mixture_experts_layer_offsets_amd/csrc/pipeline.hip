@@ -18,6 +18,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mx_device.h"
 #include "rows.h"
 
 namespace moe {
@@ -131,12 +132,14 @@ void launch_combine_list(const uint16_t *y, const float *w, const int32_t *inv,
 // f = perm[r] (token t = f / k), dy[r] = w[f] dout[t] and
 // dw[f] = <dout[t], y[r]>.  One 256-thread block per row; each lane's chunks
 // (lane, lane + 256, ...) and the final reduction follow the whole-layer
-// reverse-combine exactly, so dy and dw are bit-identical to it.
+// reverse-combine exactly, so dy and dw are bit-identical to it (and with
+// MXFP8 so are dY's codes and scales, written here as there).
 
+template <bool MXQ>
 __global__ __launch_bounds__(256) void reverse_combine_rows_kernel(
     const uint4 *__restrict__ dout, const uint4 *__restrict__ y, const float *__restrict__ w,
     const int32_t *__restrict__ perm, uint4 *__restrict__ dy, float *__restrict__ dw, int r0,
-    int k, int HC) {
+    int k, int HC, uint2 *__restrict__ dyq, uint8_t *__restrict__ dys, long rows_total) {
   __shared__ float red[4];
   const int r = r0 + blockIdx.x, tid = threadIdx.x;
   const int f = perm[r], t = f / k;
@@ -168,7 +171,13 @@ __global__ __launch_bounds__(256) void reverse_combine_rows_kernel(
           o[q] = wt * d[q];
         }
         part += s;
-        dy[(size_t)r * HC + c] = pack8(o);
+        const uint4 pk = pack8(o);
+        dy[(size_t)r * HC + c] = pk;
+        if constexpr (MXQ) {  // a quad's lanes share u and the guard
+          float vq[8];
+          unpack8(pk, vq);
+          mx_put_chunk(vq, r, c, HC, rows_total, dyq, dys);
+        }
       }
     }
   }
@@ -180,11 +189,17 @@ __global__ __launch_bounds__(256) void reverse_combine_rows_kernel(
 
 void launch_reverse_combine_rows(const uint16_t *dout, const uint16_t *y, const float *w,
                                  const int32_t *perm, uint16_t *dy, float *dw, int r0, int rows,
-                                 int k, int H, hipStream_t s) {
+                                 int k, int H, uint8_t *dyq, uint8_t *dys, long rows_total,
+                                 hipStream_t s) {
   if (rows <= 0) return;
-  hipLaunchKernelGGL(reverse_combine_rows_kernel, dim3(rows), dim3(256), 0, s,
-                     (const uint4 *)dout, (const uint4 *)y, w, perm, (uint4 *)dy, dw, r0, k,
-                     H / 8);
+  if (dyq)
+    hipLaunchKernelGGL(reverse_combine_rows_kernel<true>, dim3(rows), dim3(256), 0, s,
+                       (const uint4 *)dout, (const uint4 *)y, w, perm, (uint4 *)dy, dw, r0, k,
+                       H / 8, (uint2 *)dyq, dys, rows_total);
+  else
+    hipLaunchKernelGGL(reverse_combine_rows_kernel<false>, dim3(rows), dim3(256), 0, s,
+                       (const uint4 *)dout, (const uint4 *)y, w, perm, (uint4 *)dy, dw, r0, k,
+                       H / 8, (uint2 *)nullptr, (uint8_t *)nullptr, rows_total);
 }
 
 // ---------------------------------------------------------------------------
