@@ -291,11 +291,13 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
     rows[j] = inv[t * k + min(j, k - 1)];
     wt[j] = w[t * k + min(j, k - 1)];
   }
-  // Two chunks per lane per pass, all of a pass's loads issued before its
+  // NCH chunks per lane per pass (two; one with MXQ, whose conversion
+  // needs the registers), all of a pass's loads issued before its
   // arithmetic; partial dot products still accumulate chunk by chunk in
-  // ascending column order.
-  for (int c0 = tid; c0 < HC; c0 += 512) {
-    const bool has1 = c0 + 256 < HC;
+  // ascending column order, so dw is the same for either NCH.
+  constexpr int NCH = MXQ ? 1 : 2;
+  for (int c0 = tid; c0 < HC; c0 += 256 * NCH) {
+    const bool has1 = NCH == 2 && c0 + 256 < HC;
     // dout and the k rows of y are each read once
     const uint4 d0 = ld_once(dout + (size_t)t * HC + c0);
     const uint4 d1 = has1 ? ld_once(dout + (size_t)t * HC + c0 + 256) : make_uint4(0, 0, 0, 0);
