@@ -430,6 +430,15 @@ typedef struct moe_work_view {
   float *dec_topk_w;  /* moe_decode_fwd with a router: fp32 [T][k] weights
                          (with supplied routing the decode reads the caller's
                          arrays in place and writes none of these three) */
+  /* moe_layer_bwd with MXFP8 (NULL in bf16): the data-gradient GEMMs' MX
+     operands, each the row quantisation of the bf16 tensor above (E8M0
+     scale per 32 consecutive values of a row, [KC §02] MXFP8 backward).
+     Codes are E4M3 bytes, row-major like the bf16 tensor; scales are
+     K-blocked, block b of row r at byte (b/4 * R + r) * 4 + b%4. */
+  uint8_t *dy_codes;  /* [R][H], written by the reverse-combine */
+  uint8_t *dy_scales; /* [H/128][R][4] */
+  uint8_t *dh_codes;  /* [R][2I] */
+  uint8_t *dh_scales; /* [2I/128][R][4] */
 } moe_work_view;
 
 int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view);

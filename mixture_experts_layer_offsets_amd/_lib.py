@@ -260,7 +260,8 @@ def moe_packed_pointers(shape, packed) -> dict:
 
 class MoeWorkView(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("dy", "dh", "dx_rows", "dec_logits", "dec_topk_idx",
-                                        "dec_topk_w")]
+                                        "dec_topk_w", "dy_codes", "dy_scales", "dh_codes",
+                                        "dh_scales")]
 
 
 def moe_workspace_pointers(shape, ws) -> dict:

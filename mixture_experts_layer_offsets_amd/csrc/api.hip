@@ -1455,6 +1455,10 @@ int moe_workspace_pointers(const moe_shape *shape, void *ws, moe_work_view *view
   view->dec_logits = w.dec_logits;
   view->dec_topk_idx = w.dec_idx;
   view->dec_topk_w = w.dec_w;
+  view->dy_codes = w.dyq.q;
+  view->dy_scales = w.dyq.s;
+  view->dh_codes = w.dhq.q;
+  view->dh_scales = w.dhq.s;
   return MOE_OK;
 }
 

@@ -87,7 +87,8 @@ class MoeLayer:
 
     def work_tensor(self, name: str, dtype, shape) -> torch.Tensor:
         """A view of an intermediate left in the workspace (the backward's dy,
-        dh, dx_rows; the decode forward's dec_logits, dec_topk_idx,
+        dh, dx_rows and, with MXFP8, dy_codes, dy_scales, dh_codes,
+        dh_scales; the decode forward's dec_logits, dec_topk_idx,
         dec_topk_w), valid until the next call that uses this workspace."""
         ptr = _lib.moe_workspace_pointers(self.shape, self.ws)[name]
         if not ptr:

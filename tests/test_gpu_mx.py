@@ -161,6 +161,36 @@ def test_layer_mx_mid():
         assert np.array_equal(host(run2.grads[key]), host(v)), key
 
 
+@pytest.mark.parametrize("name,mode", [("mx-supplied-dup", m.MOE_SCHED_STAGED),
+                                       ("mx-supplied-dup", m.MOE_SCHED_PIPELINED),
+                                       ("mx-k16-router", m.MOE_SCHED_STAGED),
+                                       ("mx-shared-router", m.MOE_SCHED_PIPELINED)])
+def test_backward_mx_operands_bit_exact(name, mode):
+    """The data-gradient GEMMs' MX operands (dy written by the reverse-combine,
+    dh by the row quantiser) are the oracle's E4M3/E8M0 quantisation of the
+    bf16 dy and dh the backward stored, code for code.  The quantisation of a
+    bf16 value is decided exactly in fp32 and in fp64 (a power-of-two scale,
+    then one rounding), so the two sides must agree bit for bit."""
+    from oracle.numerics import bf16_to_f64
+    from oracle.mx import mx_quantize
+    w = MX_CASES[name]
+    note(f"MX backward operands {name} schedule {mode}: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    s = m.MoeSched()
+    s.schedule = mode
+    run = Run(w, sched=s)
+    torch.cuda.synchronize()
+    R, H, I = w.T * w.k, w.H, w.I
+    lay = run.layer
+    for name_t, cols in (("dy", H), ("dh", 2 * I)):
+        vals = bf16_to_f64(host(lay.work_tensor(name_t, torch.int16, (R, cols))).view(np.uint16))
+        codes, scales = mx_quantize(vals, axis=1)
+        got_c = host(lay.work_tensor(name_t + "_codes", torch.uint8, (R, cols)))
+        got_s = unblock_scales(host(lay.work_tensor(name_t + "_scales", torch.uint8,
+                                                    (R, cols // 32))), R, cols)
+        _assert_codes_equal(name_t + " codes", got_c, codes)
+        _assert_codes_equal(name_t + " scales", got_s, scales)
+
+
 def test_expert_ffn_entry_point_mx():
     """moe_dispatch + moe_expert_ffn + moe_combine on their own (MXFP8)."""
     w = _mx(T=400, H=384, E=6, k=4, I=256)
