@@ -193,7 +193,8 @@ __global__ __launch_bounds__(256) void quant_cols_mx_kernel(
   for (int i = 0; i < 4; i++) {
     const int chunk = tid + 256 * i, row = chunk >> 3, c8 = chunk & 7;
     const int r = r0 + row, c = c0 + 8 * c8;
-    tile[row][c8] = (r < rend && c < C) ? *(const uint4 *)(src + (size_t)r * C + c)
+    // each source row is read once in the whole backward (non-temporal)
+    tile[row][c8] = (r < rend && c < C) ? ld_once((const uint4 *)(src + (size_t)r * C + c))
                                         : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
