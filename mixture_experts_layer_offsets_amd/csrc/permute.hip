@@ -186,7 +186,9 @@ __global__ __launch_bounds__(256) void dispatch_push_mx_kernel(
       const size_t r = (size_t)row[j];
       xq[r * HC + c] = codes;
       if ((c & 3) == 0) xs[((size_t)(c >> 4) * R + r) * 4 + ((c >> 2) & 3)] = (uint8_t)sc;
-      if (xhat) xhat[r * HC + c] = hat;
+      // the round trip is read only by the backward: stored non-temporally
+      // so that it does not evict the codes the gate/up GEMM reads next
+      if (xhat) st_once(xhat + r * HC + c, hat);
     }
   }
 }
